@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for packed-thd attention and its padding mask.
+
+Test infrastructure only: imported by the tests, the package smoke check and
+the benchmark's CPU-baseline leg, never by the library itself.
+"""
+from .thd_oracle import (  # noqa: F401
+    attn_bwd,
+    attn_fwd,
+    padding_mask,
+    padding_mask_loop,
+    sequence_rows,
+    valid_pairs,
+    visible_keys,
+)
