@@ -6,6 +6,7 @@ the benchmark's CPU-baseline leg, never by the library itself.
 from .thd_oracle import (  # noqa: F401
     attn_bwd,
     attn_fwd,
+    attn_rows,
     padding_mask,
     padding_mask_loop,
     sequence_rows,

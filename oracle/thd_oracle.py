@@ -48,6 +48,7 @@ __all__ = [
     "valid_pairs",
     "attn_fwd",
     "attn_bwd",
+    "attn_rows",
 ]
 
 
@@ -277,3 +278,52 @@ def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, is_causal=None,
             dk[ok:ok + lk, hk, :] += scale * (dS.T @ Q)
             dv[ok:ok + lk, hk, :] += dV
     return dq, dk, dv
+
+
+# ---------------------------------------------------------------------------
+# Selected rows of one sequence and head (for checks at full size)
+# ---------------------------------------------------------------------------
+
+def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, is_causal=None,
+              cu_q_padded=None, cu_kv_padded=None, scale=None):
+    """Output, log-sum-exp and dq of chosen query rows of sequence b, head hq.
+
+    The same definitions as ``attn_fwd`` / ``attn_bwd`` evaluated one query row
+    at a time: row i needs only its own scores against the sequence's keys, so
+    large sequences can be checked on a sample.  ``rows`` are 0-based indices
+    inside the sequence.  Returns (out [n, d], lse [n], dq [n, d]); dq is None
+    when ``dout`` is None.
+    """
+    T_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    group = h_q // h_kv
+    scale = _default_scale(d, scale)
+    (oq, lq), = [sequence_rows(cu_q, b + 1, cu_q_padded)[b]]
+    (ok, lk), = [sequence_rows(cu_kv, b + 1, cu_kv_padded)[b]]
+    causal = bool(is_causal[b]) if is_causal is not None else False
+    hk = hq // group
+    K = np.asarray(k[ok:ok + lk, hk, :], dtype=np.float64)
+    V = np.asarray(v[ok:ok + lk, hk, :], dtype=np.float64)
+    outs, lses, dqs = [], [], []
+    for i in rows:
+        if not 0 <= i < lq:
+            raise IndexError(i)
+        qi = np.asarray(q[oq + i, hq, :], dtype=np.float64)
+        n_vis = min(i + 1, lk) if causal else lk
+        if n_vis == 0:
+            outs.append(np.zeros(d)); lses.append(-np.inf); dqs.append(np.zeros(d))
+            continue
+        s = scale * (K[:n_vis] @ qi)
+        m = s.max()
+        e = np.exp(s - m)
+        p = e / e.sum()
+        o = p @ V[:n_vis]
+        outs.append(o)
+        lses.append(m + np.log(e.sum()))
+        if dout is not None:
+            g = np.asarray(dout[oq + i, hq, :], dtype=np.float64)
+            dp = V[:n_vis] @ g
+            ds = p * (dp - (p * dp).sum())
+            dqs.append(scale * (ds @ K[:n_vis]))
+    dq = np.array(dqs) if dout is not None else None
+    return np.array(outs), np.array(lses), dq

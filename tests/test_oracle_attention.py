@@ -348,3 +348,22 @@ def test_valid_pairs_closed_form():
     w5 = workloads.config("5")
     assert valid_pairs(w5.cu_q, w5.cu_kv, w5.batch, w5.causal) == \
         int((w5.lens_q * w5.lens_kv).sum())
+
+
+def test_row_sampled_oracle_matches_whole_sequence_oracle():
+    from oracle import attn_rows
+    w = workloads.random_layout(61, batch=4, max_len=20, h_q=4, h_kv=2, d=8,
+                                dtype="bf16", causal="mixed", cross=True, min_len=0,
+                                extra_cu=2)
+    q, k, v, do = (f64(t) for t in workloads.make_tensors(w))
+    out, lse = attn_fwd(q, k, v, w.cu_q, w.cu_kv, w.batch, w.causal)
+    dq, _, _ = attn_bwd(q, k, v, do, w.cu_q, w.cu_kv, w.batch, w.causal)
+    for b, (s, n) in enumerate(sequence_rows(w.cu_q, w.batch)):
+        for hq in range(w.h_q):
+            rows = list(range(n))
+            o_r, l_r, dq_r = attn_rows(q, k, v, do, w.cu_q, w.cu_kv, b, hq, rows, w.causal)
+            if n == 0:
+                continue
+            np.testing.assert_allclose(o_r, out[s:s + n, hq], atol=1e-13)
+            np.testing.assert_allclose(l_r, lse[hq, s:s + n], atol=1e-13)
+            np.testing.assert_allclose(dq_r, dq[s:s + n, hq], atol=1e-13)

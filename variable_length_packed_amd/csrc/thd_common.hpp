@@ -1,0 +1,158 @@
+// Shared device helpers for the packed-thd attention kernels (gfx950 only).
+//
+// MFMA used throughout: v_mfma_f32_32x32x16_{bf16,f16}.  Operand layout for a
+// wave of 64 lanes, lane l, half h = l / 32, r = l % 32:
+//   A (32 x 16, M x K): lane holds A[r][8h .. 8h+7]
+//   B (16 x 32, K x N): lane holds B[8h .. 8h+7][r]
+//   C (32 x 32, M x N): lane holds C[8*(i/4) + 4h + (i%4)][r], i = 0..15
+// The K index only has to agree between A and B, so a kernel may feed any
+// fixed permutation of the 16 K values to both operands.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// Element traits: storage is 16-bit, arithmetic in fp32, MFMA in the type.
+struct Bf16 {
+  typedef __bf16 elem;
+  typedef bf16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t b) {
+    return __builtin_bit_cast(float, (uint32_t)b << 16);
+  }
+};
+
+struct Fp16 {
+  typedef _Float16 elem;
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ uint16_t bits(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+  static __device__ __forceinline__ float to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+  }
+};
+
+template <class DT>
+__device__ __forceinline__ typename DT::vec8 as_vec8(u32x4 v) {
+  return __builtin_bit_cast(typename DT::vec8, v);
+}
+
+// Pack 8 fp32 values into 8 16-bit elements (round to nearest even).
+template <class DT>
+__device__ __forceinline__ typename DT::vec8 pack8(const float* x) {
+  typename DT::vec8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (typename DT::elem)x[i];
+  return r;
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float wave_swap_halves(float x) {
+  // value held by lane l ^ 32
+  return __shfl_xor(x, 32, 64);
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int x) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    int y = __shfl_up(x, off, 64);
+    if (l >= off) x += y;
+  }
+  return x;
+}
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// Length of sequence b as the int32 difference of a cumulative buffer,
+// clamped to [0, cap] so that garbage metadata stays memory-safe.
+__device__ __forceinline__ int seq_len_clamped(const int32_t* cu, int b, int64_t cap) {
+  int64_t n = (int64_t)cu[b + 1] - (int64_t)cu[b];
+  if (n < 0) n = 0;
+  if (n > cap) n = cap;
+  return (int)n;
+}
+
+__device__ __forceinline__ int64_t seq_start(const int32_t* cu, const int32_t* cu_padded, int b) {
+  return (int64_t)(cu_padded ? cu_padded[b] : cu[b]);
+}
+
+// Map tile index t (over all sequences, in order) to (sequence, tile inside
+// the sequence) for tiles of `rows` query rows.  The whole wave participates
+// and gets the same answer.  Returns -1 when t is past the last tile.
+__device__ __forceinline__ int find_tile(const int32_t* cu, int batch, int64_t cap,
+                                         int rows, int t, int tile_cap, int* tile_in_seq) {
+  const int l = lane_id();
+  int base = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const int b = b0 + l;
+    int n = 0;
+    if (b < batch) {
+      const int len = seq_len_clamped(cu, b, cap);
+      n = (len + rows - 1) / rows;
+      if (n > tile_cap) n = tile_cap;
+    }
+    const int incl = wave_inclusive_scan(n);
+    const int total = __shfl(incl, 63, 64);
+    if (t < base + total) {
+      const uint64_t hit = __ballot(base + incl > t);
+      const int first = __builtin_ctzll(hit);
+      const int excl = __shfl(incl - n, first, 64);
+      *tile_in_seq = t - base - excl;
+      return b0 + first;
+    }
+    base += total;
+  }
+  return -1;
+}
+
+// True when row r lies inside some sequence: the last sequence whose start is
+// <= r (starts non-decreasing) must also cover r.
+__device__ __forceinline__ bool row_is_valid(const int32_t* cu, const int32_t* cu_padded,
+                                             int batch, int64_t r, int64_t cap) {
+  int lo = 0, hi = batch - 1, found = -1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    if (seq_start(cu, cu_padded, mid) <= r) {
+      found = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  if (found < 0) return false;
+  return r < seq_start(cu, cu_padded, found) + seq_len_clamped(cu, found, cap);
+}
+
+// XCD-aware remap: hardware hands consecutive workgroup ids to the 8 XCDs in
+// turn; give each XCD a contiguous range of logical ids instead so that work
+// sharing K/V (same sequence and head) shares one L2.
+__device__ __forceinline__ int xcd_remap(int b, int n) {
+  const int full = (n / 8) * 8;
+  if (b >= full) return b;
+  return (b % 8) * (full / 8) + b / 8;
+}
+
+}  // namespace thd

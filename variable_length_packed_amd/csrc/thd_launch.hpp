@@ -1,0 +1,36 @@
+// Host-side launchers shared between the C ABI layer and the kernel files.
+// All arguments have been validated by the caller; launchers only size grids
+// and enqueue kernels on the given stream.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace thd {
+
+struct Problem {
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int32_t* pad_q;   // may be null
+  const int32_t* pad_kv;  // may be null
+  const uint8_t* causal;  // may be null
+  int batch;
+  int64_t T_q, T_kv;
+  int h_q, h_kv, d;
+  float scale;
+  bool bf16;
+};
+
+hipError_t launch_padding_mask(const int32_t* cu, int batch, int max_seqlen, uint8_t* mask,
+                               hipStream_t s);
+
+hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                      float* lse, hipStream_t s);
+
+size_t bwd_workspace_bytes(const Problem& p);
+
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, hipStream_t s);
+
+}  // namespace thd
