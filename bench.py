@@ -1,0 +1,207 @@
+"""Benchmark: packed-thd attention forward + backward on one MI355X.
+
+One step = the whole hot path over one synthetic packed batch: the two
+padding masks (query and key side), thd_attn_fwd and thd_attn_bwd, all on
+the current stream with inputs already resident in HBM.  Workload: 16 causal
+sequences with lengths uniform in [64, 2048] (seed 2, 16,640 tokens), 16
+heads, head_dim 128, bf16, dO ~ N(0,1).
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+
+Prints one JSON line.  `value` is valid-pair TFLOP/s of fwd+bwd (14*d FLOPs
+per valid (query, key) pair and head); `roofline` describes the dominant
+kernel, timed with HIP events on the stream it runs on; `cpu_baseline` is the
+fp64 oracle timed on the host on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA, published
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="2")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    return ap.parse_args()
+
+
+def cpu_baseline(w, q, k, v, do, budget_s):
+    """Time the fp64 oracle (fwd + bwd) on whole heads of the workload until
+    about `budget_s` seconds of work are done; scale to valid-pair TFLOP/s."""
+    import numpy as np
+    import torch
+    from oracle import attn_bwd, attn_fwd
+    from variable_length_packed_amd.metrics import valid_pairs
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    args = (w.cu_q, w.cu_kv, w.batch, w.causal, w.cu_q_padded, w.cu_kv_padded)
+    group = w.h_q // w.h_kv
+    elapsed, heads = 0.0, 0
+    for hq in range(w.h_q):
+        hk = hq // group
+        Q = q[:, hq:hq + 1].to("cpu", torch.float64).numpy()
+        K = k[:, hk:hk + 1].to("cpu", torch.float64).numpy()
+        V = v[:, hk:hk + 1].to("cpu", torch.float64).numpy()
+        G = do[:, hq:hq + 1].to("cpu", torch.float64).numpy()
+        t0 = time.perf_counter()
+        attn_fwd(Q, K, V, *args)
+        attn_bwd(Q, K, V, G, *args)
+        elapsed += time.perf_counter() - t0
+        heads += 1
+        if elapsed >= budget_s:
+            break
+    pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, heads)
+    flops = 14 * w.d * pairs
+    return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle, fwd+bwd of {heads} of {w.h_q} heads over all "
+                      f"{w.batch} sequences of the same workload ({flops / 1e9:.1f} GFLOP in "
+                      f"{elapsed:.1f} s)"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the path shards by head or by whole sequence with no exchange, see the design "
+              "notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import variable_length_packed_amd as thd
+    import workloads
+    from variable_length_packed_amd import _lib
+    from variable_length_packed_amd.attention import _make_args, _ptr, _stream
+    from variable_length_packed_amd.metrics import attention_flops, valid_pairs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = workloads.config(a.config)
+    q, k, v, do = workloads.make_tensors(w, device=dev)
+    t32 = lambda x: None if x is None else torch.from_numpy(np.asarray(x, np.int32)).to(dev)
+    cu_q, cu_kv = t32(w.cu_q), t32(w.cu_kv)
+    pad_q, pad_kv = t32(w.cu_q_padded), t32(w.cu_kv_padded)
+    causal = torch.from_numpy(np.asarray(w.causal, np.uint8)).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty((w.h_q, w.T_q), dtype=torch.float32, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    mask_q = torch.empty((w.batch, 1, 1, w.max_seqlen_q), dtype=torch.bool, device=dev)
+    mask_kv = torch.empty((w.batch, 1, 1, w.max_seqlen_kv), dtype=torch.bool, device=dev)
+
+    lib = _lib.load()
+    args = _make_args(q, k, cu_q, cu_kv, w.max_seqlen_q, w.max_seqlen_kv, pad_q, pad_kv,
+                      causal, None, w.batch)
+    ws_bytes = int(lib.thd_attn_bwd_workspace_size(args))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    stream = _stream(dev)
+    P = {n: _ptr(t) for n, t in dict(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv,
+                                     ws=ws, cu_q=cu_q, cu_kv=cu_kv, mq=mask_q,
+                                     mkv=mask_kv).items()}
+    import ctypes
+    n_ev = 6
+    total = a.warmup + a.steps
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(total)]
+    cur = torch.cuda.current_stream(dev)
+    for evs in events:             # materialise the underlying HIP events
+        for e in evs:
+            e.record(cur)
+    torch.cuda.synchronize()
+    ev_arrays = [(ctypes.c_void_p * 4)(*[ctypes.c_void_p(e.cuda_event) for e in evs[2:6]])
+                 for evs in events]
+
+    def step(i):
+        evs = events[i]
+        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], stream),
+                   "mask q")
+        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
+                   "mask kv")
+        evs[0].record(cur)
+        _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], stream), "fwd")
+        evs[1].record(cur)
+        _lib.check(lib.thd_attn_bwd_timed(args, P["q"], P["k"], P["v"], P["o"], P["do"],
+                                          P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
+                                          ws_bytes, stream, ev_arrays[i]), "bwd")
+
+    for i in range(a.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(a.warmup, total):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    timed = events[a.warmup:]
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in timed]
+    pre_ms = [e[2].elapsed_time(e[3]) for e in timed]
+    main_ms = [e[3].elapsed_time(e[4]) for e in timed]
+    post_ms = [e[4].elapsed_time(e[5]) for e in timed]
+    mean = lambda xs: sum(xs) / len(xs)
+
+    pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, w.h_q)
+    flops = attention_flops(pairs, w.d, "fwd+bwd")
+    ms_per_step = elapsed * 1e3 / a.steps
+    value = flops / (elapsed / a.steps) / 1e12
+
+    kern = {"thd_fwd_kernel": (mean(fwd_ms), attention_flops(pairs, w.d, "fwd")),
+            "thd_bwd_main_kernel": (mean(main_ms), attention_flops(pairs, w.d, "bwd"))}
+    dom = max(kern, key=lambda n: kern[n][0])
+    dom_ms, dom_flops = kern[dom]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "avg_launch_ms": round(dom_ms, 4)}
+
+    out = {
+        "metric": "packed-THD attention valid-pair TFLOP/s fwd+bwd; % of MI355X bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": a.steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp16",
+        "data": "synthetic",
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "config": {
+            "workload": (f"packed thd self-attention, config {w.name}: {w.batch} sequences, "
+                         f"{w.T_q} tokens, h_q={w.h_q} h_kv={w.h_kv} d={w.d} {w.dtype}, "
+                         f"{int(w.causal.sum())} causal, fwd+bwd incl. both padding masks"),
+            "tokens": int(w.T_q), "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv,
+            "head_dim": w.d, "valid_pairs": int(pairs), "flops_per_step": int(flops),
+            "seed": w.seed,
+        },
+        "kernel_ms": {"fwd": round(mean(fwd_ms), 4), "bwd_pre": round(mean(pre_ms), 4),
+                      "bwd_main": round(mean(main_ms), 4), "bwd_post": round(mean(post_ms), 4)},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -129,6 +129,17 @@ int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k,
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                  void* stream);
 
+/* thd_attn_bwd with timing marks: the same validation and launches, plus
+ * hipEventRecord of events[0..3] (four hipEvent_t created by the caller) on
+ * `stream` before the row-statistics pass, before the main gradient kernel,
+ * before the conversion pass and after it, so that a caller can time each
+ * kernel on the stream it runs on.  Errors: as thd_attn_bwd, THD_ERR_NULL if
+ * an event is missing, THD_ERR_HIP if recording fails. */
+int thd_attn_bwd_timed(const thd_varlen_args* args, const void* q, const void* k,
+                       const void* v, const void* o, const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* events);
+
 /* Static string naming a status code. */
 const char* thd_status_string(int status);
 

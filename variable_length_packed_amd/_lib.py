@@ -29,6 +29,7 @@ EXPORTED = (
     "thd_attn_fwd",
     "thd_attn_bwd_workspace_size",
     "thd_attn_bwd",
+    "thd_attn_bwd_timed",
     "thd_status_string",
     "thd_version",
 )
@@ -85,6 +86,9 @@ def load(path=None):
     lib.thd_attn_bwd_workspace_size.restype = sz
     lib.thd_attn_bwd.argtypes = [argsp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.thd_attn_bwd.restype = ctypes.c_int
+    lib.thd_attn_bwd_timed.argtypes = [argsp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                       ctypes.POINTER(vp)]
+    lib.thd_attn_bwd_timed.restype = ctypes.c_int
     lib.thd_status_string.argtypes = [ctypes.c_int]
     lib.thd_status_string.restype = ctypes.c_char_p
     lib.thd_version.argtypes = []

@@ -105,9 +105,10 @@ size_t thd_attn_bwd_workspace_size(const thd_varlen_args* args) {
   return thd::bwd_workspace_bytes(p);
 }
 
-int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k, const void* v,
-                 const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                 void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+static int attn_bwd_impl(const thd_varlen_args* args, const void* q, const void* k,
+                         const void* v, const void* o, const void* dout, const float* lse,
+                         void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                         void* stream, void* const* events) {
   thd::Problem p;
   int st = to_problem(args, &p);
   if (st != THD_OK) return st;
@@ -124,8 +125,24 @@ int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k, cons
     if (((uintptr_t)workspace & 255u) != 0) return THD_ERR_WORKSPACE;
   }
   hipError_t e = thd::launch_bwd(p, q, k, v, o, dout, lse, dq, dk, dv, workspace,
-                                 (hipStream_t)stream);
+                                 (hipStream_t)stream, (hipEvent_t const*)events);
   return e == hipSuccess ? THD_OK : THD_ERR_HIP;
+}
+
+int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k, const void* v,
+                 const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                 void* dv, void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_bwd_impl(args, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                       stream, nullptr);
+}
+
+int thd_attn_bwd_timed(const thd_varlen_args* args, const void* q, const void* k,
+                       const void* v, const void* o, const void* dout, const float* lse,
+                       void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                       void* stream, void* const* events) {
+  if (!events || !events[0] || !events[1] || !events[2] || !events[3]) return THD_ERR_NULL;
+  return attn_bwd_impl(args, q, k, v, o, dout, lse, dq, dk, dv, workspace, workspace_bytes,
+                       stream, events);
 }
 
 }  // extern "C"

@@ -454,7 +454,12 @@ __global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int64_t 
 }
 
 template <class DT, int DP>
-hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev) {
+  auto mark = [&](int i) -> hipError_t {
+    return ev ? hipEventRecord(ev[i], s) : hipSuccess;
+  };
+  hipError_t em = mark(0);
+  if (em != hipSuccess) return em;
   const int64_t pairs = bp.T_q * bp.h_q;
   if (pairs > 0) {
     hipLaunchKernelGGL((thd_bwd_pre_kernel<DT>), dim3((unsigned)((pairs + 15) / 16)), dim3(256),
@@ -462,20 +467,23 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s) {
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if ((em = mark(1)) != hipSuccess) return em;
   if (bp.n_main > 0) {
     hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(256), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if ((em = mark(2)) != hipSuccess) return em;
   const int64_t n_chunks = bp.T_q * bp.h_q * bp.d / 8;
   const int64_t n_conv = (n_chunks + 255) / 256;
   const int64_t n_zero = (bp.T_kv + kZeroRowsB - 1) / kZeroRowsB;
   if (n_conv + n_zero > 0) {
     hipLaunchKernelGGL((thd_bwd_post_kernel<DT>), dim3((unsigned)(n_conv + n_zero)), dim3(256), 0,
                        s, bp, n_chunks, (int)n_conv);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-  return hipSuccess;
+  return mark(3);
 }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -490,7 +498,7 @@ size_t bwd_workspace_bytes(const Problem& p) {
 
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                      void* dv, void* workspace, hipStream_t s) {
+                      void* dv, void* workspace, hipStream_t s, hipEvent_t const* ev) {
   BwdParams bp;
   bp.q = (const uint16_t*)q;
   bp.k = (const uint16_t*)k;
@@ -520,9 +528,9 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   const int64_t n_kv_tiles = (p.T_kv + kBwdBK - 1) / kBwdBK + p.batch;
   bp.n_kv_tiles = (int)n_kv_tiles;
   bp.n_main = (p.batch > 0) ? (int)(n_kv_tiles * p.h_kv) : 0;
-  if (p.d <= 32) return p.bf16 ? launch_bwd_t<Bf16, 32>(bp, s) : launch_bwd_t<Fp16, 32>(bp, s);
-  if (p.d <= 64) return p.bf16 ? launch_bwd_t<Bf16, 64>(bp, s) : launch_bwd_t<Fp16, 64>(bp, s);
-  return p.bf16 ? launch_bwd_t<Bf16, 128>(bp, s) : launch_bwd_t<Fp16, 128>(bp, s);
+  if (p.d <= 32) return p.bf16 ? launch_bwd_t<Bf16, 32>(bp, s, ev) : launch_bwd_t<Fp16, 32>(bp, s, ev);
+  if (p.d <= 64) return p.bf16 ? launch_bwd_t<Bf16, 64>(bp, s, ev) : launch_bwd_t<Fp16, 64>(bp, s, ev);
+  return p.bf16 ? launch_bwd_t<Bf16, 128>(bp, s, ev) : launch_bwd_t<Fp16, 128>(bp, s, ev);
 }
 
 }  // namespace thd

@@ -29,8 +29,11 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
 
 size_t bwd_workspace_bytes(const Problem& p);
 
+// `events` is null or four events recorded on `s` before the pre pass, before
+// the main kernel, before the post pass and after it.
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
-                      void* dv, void* workspace, hipStream_t s);
+                      void* dv, void* workspace, hipStream_t s,
+                      hipEvent_t const* events = nullptr);
 
 }  // namespace thd
