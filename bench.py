@@ -35,7 +35,22 @@ def parse():
     ap.add_argument("--config", default="2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (read + write) a few "
+                         "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    """A plain copy kernel of known size: reads and writes exactly mib MiB."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(f'{{"copy_calibration_bytes": {n * 4}}}', flush=True)
 
 
 def cpu_baseline(w, q, k, v, do, budget_s):
@@ -77,6 +92,9 @@ def cpu_baseline(w, q, k, v, do, budget_s):
 
 def main():
     a = parse()
+    if a.copy_calibration_mib:
+        copy_calibration(a.copy_calibration_mib)
+        return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
               "(the path shards by head or by whole sequence with no exchange, see the design "

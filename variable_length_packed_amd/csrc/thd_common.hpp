@@ -86,6 +86,49 @@ __device__ __forceinline__ int wave_inclusive_scan(int x) {
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// ---------------------------------------------------------------------------
+// Raw buffer access.  A buffer resource covers one sequence's rows of one
+// head: base = its first element, num_records = rows * row_bytes.  Loads past
+// num_records return zeros and stores / atomics past it are dropped, which is
+// how rows beyond a sequence's length are handled without per-access checks.
+// Offsets are 32-bit, so every resource is kept below 2^31 bytes.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 raw buffer format word
+constexpr uint32_t kOobOffset = 0x80000000u;  // any offset >= num_records reads 0
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRsrcWord3);
+}
+
+__device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+
+__device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ void buf_store4(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)voff, (int)soff, 0);
+}
+
+// Rows of a sequence that may be touched: [start, start + n) intersected with
+// [0, T), and few enough that n * row_bytes stays below 2^31.
+__device__ __forceinline__ int clamp_rows(int64_t start, int len, int64_t T, int64_t row_bytes) {
+  if (start < 0 || start >= T || len <= 0) return 0;
+  int64_t n = len;
+  if (n > T - start) n = T - start;
+  const int64_t cap = ((int64_t)1 << 31) / row_bytes - 1;
+  if (n > cap) n = cap;
+  return (int)n;
+}
+
 // Length of sequence b as the int32 difference of a cumulative buffer,
 // clamped to [0, cap] so that garbage metadata stays memory-safe.
 __device__ __forceinline__ int seq_len_clamped(const int32_t* cu, int b, int64_t cap) {

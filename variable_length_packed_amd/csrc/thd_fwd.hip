@@ -82,8 +82,13 @@ __device__ void fwd_zero_pad_rows(const FwdParams& p, int zb) {
   }
 }
 
+// Threshold (log2 units) by which a row maximum must grow before the running
+// maximum is moved and the accumulator rescaled; below it the stale maximum
+// stays, probabilities may reach 2^8, which fp32 sums and 16-bit P hold.
+constexpr float kRescaleLog2 = 8.0f;
+
 template <class DT, int DP>
-__global__ __launch_bounds__(256) void thd_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
   constexpr int KST = DP + 8;      // LDS row stride of K (elements)
   constexpr int VST = BN + 8;      // LDS row stride of V^T (elements)
@@ -92,20 +97,23 @@ __global__ __launch_bounds__(256) void thd_fwd_kernel(FwdParams p) {
   constexpr int KCH = DP / 8;      // 16-byte chunks per K row
   constexpr int KLOADS = BN * KCH / 256;
   constexpr int VTHREADS = 2 * DP; // 16 key groups x DP/8 chunks
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[DP * VST];
+  constexpr int KBUF = BN * KST, VBUF = DP * VST;
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
 
   const int bid = blockIdx.x;
   if (bid >= p.n_attn) {
     fwd_zero_pad_rows(p, bid - p.n_attn);
     return;
   }
+  // Heaviest work first: within a head, walk query tiles from the last one.
   const int logical = xcd_remap(bid, p.n_attn);
   const int hq = logical / p.n_tiles;
-  const int t = logical - hq * p.n_tiles;
+  const int t = p.n_tiles - 1 - (logical - hq * p.n_tiles);
   int tile_in_seq = 0;
-  const int b = find_tile(p.cu_q, p.batch, p.T_q, BM, t, p.n_tiles, &tile_in_seq);
+  const int b = uniform(find_tile(p.cu_q, p.batch, p.T_q, BM, t, p.n_tiles, &tile_in_seq));
   if (b < 0) return;
+  tile_in_seq = uniform(tile_in_seq);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -113,83 +121,83 @@ __global__ __launch_bounds__(256) void thd_fwd_kernel(FwdParams p) {
   const int r = l & 31;
   const int h = l >> 5;
 
-  const int lq = seq_len_clamped(p.cu_q, b, p.T_q);
-  const int lk = seq_len_clamped(p.cu_kv, b, p.T_kv);
+  const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
+  const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
   const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
   const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, qrow_bytes));
+  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
   const bool causal = p.causal ? (p.causal[b] != 0) : false;
   const int hk = hq / p.group;
   const int q0 = tile_in_seq * BM;
+  if (q0 >= lq) return;
   const int qw0 = q0 + w * kWaveM;
   const int my_q = qw0 + r;
-  const int64_t q_stride = (int64_t)p.h_q * p.d;
-  const int64_t kv_stride = (int64_t)p.h_kv * p.d;
 
   int kv_end = lk;
   if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
   const int n_kv_tiles = (kv_end + BN - 1) / BN;
 
+  // Resources: this sequence's rows of head hq (q, o) and of head hk (k, v).
+  const uint16_t* qbase = p.q + sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
+  uint16_t* obase = p.o + sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
+  const rsrc_t q_rs = make_rsrc(qbase, (uint32_t)lq * qrow_bytes);
+  const rsrc_t o_rs = make_rsrc(obase, (uint32_t)lq * qrow_bytes);
+  const char* kbase = (const char*)(p.k + sk * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d);
+  const char* vbase = (const char*)(p.v + sk * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d);
+
   // Q as the B operand of S^T = K Q^T: lane holds Q[my_q][16c + 8h .. +7].
   typename DT::vec8 qreg[NC];
-  {
-    const int64_t row = sq + my_q;
-    const bool ok = my_q < lq && row >= 0 && row < p.T_q;
-    const uint16_t* src = p.q + row * q_stride + (int64_t)hq * p.d;
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int dd = 16 * c + 8 * h;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ok && dd < p.d) x = *(const u32x4*)(src + dd);
-      qreg[c] = as_vec8<DT>(x);
-    }
+  for (int c = 0; c < NC; ++c) {
+    const int dd = 16 * c + 8 * h;
+    const uint32_t off = dd < p.d ? (uint32_t)my_q * qrow_bytes + 2u * dd : kOobOffset;
+    qreg[c] = as_vec8<DT>(buf_load16(q_rs, off, 0));
   }
 
   f32x16 acc[ND];
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
-  float m_run = -__builtin_inff();
-  float l_run = 0.f;
+  float m_run = -__builtin_inff();  // running max of the raw scores (stale up to 2^8)
+  float l_run = 0.f;                // this lane's share of the row sum
 
-  // Global -> register staging of one K/V tile.
+  // Per-thread offsets of the K / V chunks it stages (relative to a tile).
+  uint32_t koff[KLOADS];
+#pragma unroll
+  for (int i = 0; i < KLOADS; ++i) {
+    const int cid = tid + 256 * i;
+    const int row = cid / KCH;
+    const int c = cid - row * KCH;
+    koff[i] = 8 * c < p.d ? (uint32_t)row * kvrow_bytes + 16u * c : kOobOffset;
+  }
+  const int v_grp = tid & 15;    // key group of 4 keys
+  const int v_chunk = tid >> 4;  // 8-wide d chunk
+  const uint32_t voff0 = 8 * v_chunk < p.d && tid < VTHREADS
+                             ? (uint32_t)(4 * v_grp) * kvrow_bytes + 16u * v_chunk
+                             : kOobOffset;
+
   u32x4 kreg[KLOADS];
   u32x4 vreg[4];
-  const int v_grp = tid & 15;   // key group of 4 keys
-  const int v_chunk = tid >> 4; // 8-wide d chunk
-  const uint16_t* kbase = p.k + (int64_t)hk * p.d;
-  const uint16_t* vbase = p.v + (int64_t)hk * p.d;
-
   auto load_tile = [&](int k0) {
+    const uint32_t left = (uint32_t)(lk - k0);  // >= 1 for every tile we visit
+    const rsrc_t k_rs = make_rsrc(kbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const rsrc_t v_rs = make_rsrc(vbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int cid = tid + 256 * i;
-      const int row = cid / KCH;
-      const int c = cid - row * KCH;
-      const int j = k0 + row;
-      const int64_t g = sk + j;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < lk && g >= 0 && g < p.T_kv && 8 * c < p.d) x = *(const u32x4*)(kbase + g * kv_stride + 8 * c);
-      kreg[i] = x;
-    }
-    if (tid < VTHREADS) {
+    for (int i = 0; i < KLOADS; ++i) kreg[i] = buf_load16(k_rs, koff[i], 0);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = k0 + 4 * v_grp + i;
-        const int64_t g = sk + j;
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (j < lk && g >= 0 && g < p.T_kv && 8 * v_chunk < p.d)
-          x = *(const u32x4*)(vbase + g * kv_stride + 8 * v_chunk);
-        vreg[i] = x;
-      }
-    }
+    for (int i = 0; i < 4; ++i)
+      vreg[i] = buf_load16(v_rs, voff0 == kOobOffset ? kOobOffset : voff0 + i * kvrow_bytes, 0);
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int buf) {
+    uint16_t* Kb = Ks + buf * KBUF;
+    uint16_t* Vb = Vt + buf * VBUF;
 #pragma unroll
     for (int i = 0; i < KLOADS; ++i) {
       const int cid = tid + 256 * i;
       const int row = cid / KCH;
       const int c = cid - row * KCH;
-      *(u32x4*)(&Ks[row * KST + 8 * c]) = kreg[i];
+      *(u32x4*)(&Kb[row * KST + 8 * c]) = kreg[i];
     }
     if (tid < VTHREADS) {
       // 4 keys x 8 d  ->  8 rows of V^T with 4 keys each
@@ -197,124 +205,132 @@ __global__ __launch_bounds__(256) void thd_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int word = e >> 1;
-        const bool hi = e & 1;
-        uint32_t x0 = vreg[0][word], x1 = vreg[1][word], x2 = vreg[2][word], x3 = vreg[3][word];
+        const uint32_t x0 = vreg[0][word], x1 = vreg[1][word], x2 = vreg[2][word],
+                       x3 = vreg[3][word];
         u32x2 out;
-        if (!hi) {
-          out[0] = (x0 & 0xffffu) | (x1 << 16);
-          out[1] = (x2 & 0xffffu) | (x3 << 16);
+        if (!(e & 1)) {
+          out[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
+          out[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
         } else {
-          out[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-          out[1] = (x2 >> 16) | (x3 & 0xffff0000u);
+          out[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
+          out[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
         }
-        *(u32x2*)(&Vt[(8 * v_chunk + e) * VST + pos]) = out;
+        *(u32x2*)(&Vb[(8 * v_chunk + e) * VST + pos]) = out;
       }
     }
   };
 
-  if (n_kv_tiles > 0) load_tile(0);
+  const float c2 = p.c2;
+  if (n_kv_tiles > 0) {
+    load_tile(0);
+    store_tile(0);
+  }
+  __syncthreads();
   for (int it = 0; it < n_kv_tiles; ++it) {
     const int k0 = it * BN;
-    __syncthreads();
-    store_tile();
-    __syncthreads();
-    if (it + 1 < n_kv_tiles) load_tile(k0 + BN);
+    const int buf = it & 1;
+    const bool more = it + 1 < n_kv_tiles;
+    if (more) load_tile(k0 + BN);
 
     const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + kWaveM - 1);
-    if (!active) continue;
-
-    // S^T tiles: rows = keys k0 + 32*tt + (C row), columns = this wave's queries
-    f32x16 s[2];
+    if (active) {
+      const uint16_t* Kb = Ks + buf * KBUF;
+      const uint16_t* Vb = Vt + buf * VBUF;
+      // S^T tiles: rows = keys k0 + 32*tt + (C row), columns = this wave's queries
+      f32x16 s[2];
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
-      s[tt] = f32x16{};
+      for (int tt = 0; tt < 2; ++tt) {
+        s[tt] = f32x16{};
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 a = *(const u32x4*)(&Ks[(32 * tt + r) * KST + 16 * c + 8 * h]);
-        s[tt] = DT::mfma(as_vec8<DT>(a), qreg[c], s[tt]);
+        for (int c = 0; c < NC; ++c) {
+          const u32x4 a = *(const u32x4*)(&Kb[(32 * tt + r) * KST + 16 * c + 8 * h]);
+          s[tt] = DT::mfma(as_vec8<DT>(a), qreg[c], s[tt]);
+        }
       }
-    }
 
-    const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
-    if (need_mask) {
+      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+      if (need_mask) {
+        const int lim = causal ? (my_q + 1 < lk ? my_q + 1 : lk) : lk;  // keys j < lim visible
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int j = k0 + 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (j >= lim) s[tt][i] = -__builtin_inff();
+          }
+      }
+
+      float mt = -__builtin_inff();
+#pragma unroll
+      for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
+      mt = fmaxf(mt, wave_swap_halves(mt));
+      // Move the running max only when it grew by more than 2^8 in exp2 units.
+      const bool grow = mt != -__builtin_inff() &&
+                        (m_run == -__builtin_inff() || (mt - m_run) * c2 > kRescaleLog2);
+      if (__builtin_amdgcn_ballot_w64(grow)) {
+        const float m_new = grow ? mt : m_run;
+        const float alpha = grow ? __builtin_amdgcn_exp2f((m_run - m_new) * c2) : 1.f;
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int j = k0 + 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
-          const bool vis = (j < lk) && (!causal || j <= my_q);
-          if (!vis) s[tt][i] = -__builtin_inff();
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, -mc));
+          s[tt][i] = e;
+          l_run += e;
         }
-    }
 
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
-    mt = fmaxf(mt, wave_swap_halves(mt));
-    const float m_new = fmaxf(m_run, mt);
-    const float mc = (m_new == -__builtin_inff()) ? 0.f : m_new * p.c2;
-    const float alpha = __builtin_amdgcn_exp2f(m_run * p.c2 - mc);
-    float ps = 0.f;
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], p.c2, -mc));
-        s[tt][i] = e;
-        ps += e;
-      }
-    l_run = l_run * alpha + ps;
-    m_run = m_new;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[dt][i] *= alpha;
-
-    typename DT::vec8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      float tmp[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) tmp[j] = s[kb >> 1][8 * (kb & 1) + j];
-      pb[kb] = pack8<DT>(tmp);
-    }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+      typename DT::vec8 pb[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        const u32x4 a = *(const u32x4*)(&Vt[(32 * dt + r) * VST + 16 * kb + 8 * h]);
-        acc[dt] = DT::mfma(as_vec8<DT>(a), pb[kb], acc[dt]);
+        float tmp[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) tmp[j] = s[kb >> 1][8 * (kb & 1) + j];
+        pb[kb] = pack8<DT>(tmp);
       }
-  }
-
-  // Epilogue: O = acc / l, LSE = m * scale + ln(l).
-  const float lt = l_run + wave_swap_halves(l_run);
-  if (my_q < lq) {
-    const int64_t row = sq + my_q;
-    if (row >= 0 && row < p.T_q) {
-      const float inv = lt > 0.f ? 1.f / lt : 0.f;
-      uint16_t* dst = p.o + row * q_stride + (int64_t)hq * p.d;
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int dd = 32 * dt + 8 * g + 4 * h;
-          if (dd < p.d) {
-            u32x2 out;
-            out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * inv) |
-                     ((uint32_t)DT::bits(acc[dt][4 * g + 1] * inv) << 16);
-            out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * inv) |
-                     ((uint32_t)DT::bits(acc[dt][4 * g + 3] * inv) << 16);
-            *(u32x2*)(dst + dd) = out;
-          }
+        for (int kb = 0; kb < 4; ++kb) {
+          const u32x4 a = *(const u32x4*)(&Vb[(32 * dt + r) * VST + 16 * kb + 8 * h]);
+          acc[dt] = DT::mfma(as_vec8<DT>(a), pb[kb], acc[dt]);
         }
-      if (h == 0)
-        p.lse[(int64_t)hq * p.T_q + row] =
-            lt > 0.f ? m_run * p.scale + __logf(lt) : -__builtin_inff();
     }
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
   }
+
+  // Epilogue: O = acc / l, LSE = m * scale + ln(l).  Rows past lq are dropped
+  // by the resource bound.
+  const float lt = l_run + wave_swap_halves(l_run);
+  const float inv = lt > 0.f ? 1.f / lt : 0.f;
+  const uint32_t orow = (uint32_t)my_q * qrow_bytes;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int dd = 32 * dt + 8 * g + 4 * h;
+      if (dd < p.d) {
+        u32x2 out;
+        out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * inv) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 1] * inv) << 16);
+        out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * inv) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 3] * inv) << 16);
+        buf_store8(out, o_rs, orow + 2u * dd, 0);
+      }
+    }
+  if (h == 0 && my_q < lq)
+    p.lse[(int64_t)hq * p.T_q + sq + my_q] =
+        lt > 0.f ? m_run * p.scale + __logf(lt) : -__builtin_inff();
 }
 
 template <class DT, int DP>
