@@ -36,6 +36,9 @@ def compile_flags():
         "-Wno-unused-function",
         # keep hipcc from forming packed fp32 ops on its own
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in VGPRs: the softmax / gradient VALU work reads them
+        # directly instead of copying them out of AGPRs
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]

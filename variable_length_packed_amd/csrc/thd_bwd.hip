@@ -54,10 +54,6 @@ struct BwdParams {
   int n_main;      // n_kv_tiles * h_kv
 };
 
-__device__ __forceinline__ int tr_group_pos(int g4) {
-  return (g4 == 1) ? 2 : (g4 == 2) ? 1 : g4;
-}
-
 // ---------------------------------------------------------------------------
 // pre: D = rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
 // ---------------------------------------------------------------------------
@@ -95,185 +91,146 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // main
 // ---------------------------------------------------------------------------
+// LDS: the K tile [BK][DP] (resident), two buffers of the query tile (Q and
+// dO [BQ][DP], LSE and D [BQ]) and dS [BQ][BK] (padded rows).  Q, dO and K
+// are stored row-major (swizzled); their transposes for dV^T = dO^T P,
+// dK^T = Q^T dS and dQ = dS K come from transpose reads.
 template <class DT, int DP>
-__global__ __launch_bounds__(256) void thd_bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int BK = kBwdBK, BQ = kBwdBQ;
   constexpr int NC = DP / 16;
   constexpr int ND = DP / 32;
-  constexpr int RST = DP + 8;   // row-major Q / dO / K-staging stride
-  constexpr int TST = BQ + 8;   // transposed Q / dO stride
-  constexpr int SST = BK + 8;   // dS stride
   constexpr int KCH = DP / 8;
-  constexpr int OFF_QS = 0;
-  constexpr int OFF_DOS = OFF_QS + BQ * RST * 2;
-  constexpr int OFF_QT = OFF_DOS + BQ * RST * 2;
-  constexpr int OFF_DOT = OFF_QT + DP * TST * 2;
-  constexpr int OFF_DS = OFF_DOT + DP * TST * 2;
-  constexpr int OFF_LSE = OFF_DS + BQ * SST * 2;
-  constexpr int OFF_D = OFF_LSE + BQ * 4;
-  constexpr int SMEM = OFF_D + BQ * 4;
-  constexpr int KSTAGE = BK * RST * 2;
-  static_assert(KSTAGE <= OFF_DS, "K staging must fit below the dS region");
+  constexpr int SST = BK + 8;   // dS row stride (elements)
+  constexpr int TILE = BQ * DP * 2;
+  constexpr int OFF_K = 0;
+  constexpr int OFF_Q = OFF_K + BK * DP * 2;
+  constexpr int OFF_DO = OFF_Q + 2 * TILE;
+  constexpr int OFF_LSE = OFF_DO + 2 * TILE;
+  constexpr int OFF_D = OFF_LSE + 2 * BQ * 4;
+  constexpr int OFF_DS = OFF_D + 2 * BQ * 4;
+  constexpr int SMEM = OFF_DS + BQ * SST * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  uint16_t* Qs = (uint16_t*)(smem + OFF_QS);
-  uint16_t* dOs = (uint16_t*)(smem + OFF_DOS);
-  uint16_t* Qt = (uint16_t*)(smem + OFF_QT);
-  uint16_t* dOt = (uint16_t*)(smem + OFF_DOT);
+  unsigned char* Kt = smem + OFF_K;
   uint16_t* dSs = (uint16_t*)(smem + OFF_DS);
-  float* lse2s = (float*)(smem + OFF_LSE);
-  float* dds = (float*)(smem + OFF_D);
-  uint16_t* Kst = (uint16_t*)smem;  // aliases the query-tile buffers at start
 
   const int bid = blockIdx.x;
   const int logical = xcd_remap(bid, p.n_main);
   const int hk = logical / p.n_kv_tiles;
   const int t = logical - hk * p.n_kv_tiles;
   int tile_in_seq = 0;
-  const int b = find_tile(p.cu_kv, p.batch, p.T_kv, BK, t, p.n_kv_tiles, &tile_in_seq);
+  const int b = uniform(find_tile(p.cu_kv, p.batch, p.T_kv, BK, t, p.n_kv_tiles, &tile_in_seq));
   if (b < 0) return;
+  tile_in_seq = uniform(tile_in_seq);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
   const int l = tid & 63;
   const int r = l & 31;
   const int h = l >> 5;
+  const int g16 = l & 15;        // lane inside its 16-lane group
+  const int grp = l >> 4;        // 16-lane group of the wave
 
-  const int lq = seq_len_clamped(p.cu_q, b, p.T_q);
-  const int lk = seq_len_clamped(p.cu_kv, b, p.T_kv);
+  const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
+  const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
+  const uint32_t accrow_bytes = (uint32_t)p.h_q * p.d * 4;
   const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
   const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
+  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
   const bool causal = p.causal ? (p.causal[b] != 0) : false;
   const int k0 = tile_in_seq * BK;
+  if (k0 >= lk) return;
   const int kw0 = k0 + 32 * w;
   const int my_k = kw0 + r;
-  const int64_t q_stride = (int64_t)p.h_q * p.d;
-  const int64_t kv_stride = (int64_t)p.h_kv * p.d;
 
-  // K and V of this lane's key as B operands (S = Q K^T, dP = dO V^T).
-  typename DT::vec8 kB[NC], vB[NC];
-  {
-    const int64_t g = sk + my_k;
-    const bool ok = my_k < lk && g >= 0 && g < p.T_kv;
-    const uint16_t* ks = p.k + g * kv_stride + (int64_t)hk * p.d;
-    const uint16_t* vs = p.v + g * kv_stride + (int64_t)hk * p.d;
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int dd = 16 * c + 8 * h;
-      u32x4 xk = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
-      if (ok && dd < p.d) {
-        xk = *(const u32x4*)(ks + dd);
-        xv = *(const u32x4*)(vs + dd);
-      }
-      kB[c] = as_vec8<DT>(xk);
-      vB[c] = as_vec8<DT>(xv);
-    }
-  }
+  // Keys [k0, lk) of kv head hk; rows past lk read as zeros.
+  const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
+  const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
+  const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
+  const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
+  const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
 
-  // K of the whole tile as the B operand of dQ = dS K for d columns
-  // 32w .. 32w+31: lane holds K[16kb + 8h + j][32w + r], staged via LDS.
-  typename DT::vec8 kA[BK / 16];
-  {
+  // K tile -> LDS (row-major, swizzled).
 #pragma unroll
-    for (int i = 0; i < BK * KCH / 256; ++i) {
-      const int cid = tid + 256 * i;
-      const int row = cid / KCH;
-      const int c = cid - row * KCH;
-      const int j = k0 + row;
-      const int64_t g = sk + j;
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (j < lk && g >= 0 && g < p.T_kv && 8 * c < p.d)
-        x = *(const u32x4*)(p.k + g * kv_stride + (int64_t)hk * p.d + 8 * c);
-      *(u32x4*)(&Kst[row * RST + 8 * c]) = x;
-    }
-    __syncthreads();
-    if (w < ND) {
-#pragma unroll
-      for (int kb = 0; kb < BK / 16; ++kb) {
-        uint16_t e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = Kst[(16 * kb + 8 * h + j) * RST + 32 * w + r];
-        u32x4 x;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] = (uint32_t)e[2 * j] | ((uint32_t)e[2 * j + 1] << 16);
-        kA[kb] = as_vec8<DT>(x);
-      }
-    }
+  for (int i = 0; i < BK * KCH / 256; ++i) {
+    const int cid = tid + 256 * i;
+    const int row = cid / KCH;
+    const int x = cid - row * KCH;
+    const uint32_t off = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
+    *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, off, 0);
   }
+  // V of this lane's key as the B operand of dP = dO V^T.
+  typename DT::vec8 vB[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int dd = 16 * c + 8 * h;
+    const uint32_t off = dd < p.d ? (uint32_t)(32 * w + r) * kvrow_bytes + 2u * dd : kOobOffset;
+    vB[c] = as_vec8<DT>(buf_load16(v_rs, off, 0));
+  }
+  __syncthreads();
+  // K of this lane's key as the B operand of S = Q K^T (from the LDS tile).
+  typename DT::vec8 kB[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    kB[c] = as_vec8<DT>(*(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h)));
 
   // Query tiles: from the first tile that can see key k0 when causal.
   const int q_start = causal ? (k0 / BQ) * BQ : 0;
   const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
   const int n_iter = p.group * n_qt;
 
-  // Staging of one query tile: thread t < DP loads 4 rows x 8 d of Q and dO;
-  // threads 224..255 load LSE and D.
-  const int s_grp = tid & 7;    // group of 4 query rows
-  const int s_chunk = tid >> 3; // 8-wide d chunk
-  u32x4 qreg[4], oreg[4];
+  // Staging of one query tile: BQ*KCH chunks of Q and of dO; threads
+  // 256-BQ .. 255 also fetch LSE and D.
+  constexpr int QLOADS = (BQ * KCH + 255) / 256;
+  const int st_lane = tid - (256 - BQ);
+  u32x4 qreg[QLOADS], oreg[QLOADS];
   float lse_r = 0.f, d_r = 0.f;
 
-  auto load_q = [&](int iter) {
-    const int hq = hk * p.group + iter / n_qt;
-    const int q0 = q_start + (iter % n_qt) * BQ;
-    if (tid < DP) {
+  auto load_q = [&](int hq, int q0) {
+    const int64_t hoff = sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
+    const rsrc_t q_rs = make_rsrc(p.q + hoff, (uint32_t)lq * qrow_bytes);
+    const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int qi = q0 + 4 * s_grp + i;
-        const int64_t g = sq + qi;
-        u32x4 xq = {0u, 0u, 0u, 0u}, xo = {0u, 0u, 0u, 0u};
-        if (qi < lq && g >= 0 && g < p.T_q && 8 * s_chunk < p.d) {
-          const int64_t off = g * q_stride + (int64_t)hq * p.d + 8 * s_chunk;
-          xq = *(const u32x4*)(p.q + off);
-          xo = *(const u32x4*)(p.dout + off);
-        }
-        qreg[i] = xq;
-        oreg[i] = xo;
-      }
+    for (int i = 0; i < QLOADS; ++i) {
+      const int cid = tid + 256 * i;
+      const int row = cid / KCH;
+      const int x = cid - row * KCH;
+      const uint32_t off = (cid < BQ * KCH && 8 * x < p.d)
+                               ? (uint32_t)(q0 + row) * qrow_bytes + 16u * x
+                               : kOobOffset;
+      qreg[i] = buf_load16(q_rs, off, 0);
+      oreg[i] = buf_load16(o_rs, off, 0);
     }
-    if (tid >= 256 - BQ) {
-      const int qi = q0 + tid - (256 - BQ);
-      const int64_t g = sq + qi;
-      if (qi < lq && g >= 0 && g < p.T_q) {
-        lse_r = p.lse[(int64_t)hq * p.T_q + g] * kLog2e;
-        d_r = p.dsum[(int64_t)hq * p.T_q + g];
+    if (st_lane >= 0) {
+      const int qi = q0 + st_lane;
+      if (qi < lq) {
+        const int64_t idx = (int64_t)hq * p.T_q + sq + qi;
+        lse_r = p.lse[idx] * kLog2e;
+        d_r = p.dsum[idx];
       } else {
-        lse_r = __builtin_inff();
+        lse_r = __builtin_inff();  // rows past the sequence get P = 0
         d_r = 0.f;
       }
     }
   };
 
-  auto store_transposed = [&](uint16_t* dstT, const u32x4* src) {
-    const int pos = 16 * (s_grp >> 2) + 4 * tr_group_pos(s_grp & 3);
+  auto store_q = [&](int buf) {
+    unsigned char* Qb = smem + OFF_Q + buf * TILE;
+    unsigned char* Ob = smem + OFF_DO + buf * TILE;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int word = e >> 1;
-      const uint32_t x0 = src[0][word], x1 = src[1][word], x2 = src[2][word], x3 = src[3][word];
-      u32x2 out;
-      if (!(e & 1)) {
-        out[0] = (x0 & 0xffffu) | (x1 << 16);
-        out[1] = (x2 & 0xffffu) | (x3 << 16);
-      } else {
-        out[0] = (x0 >> 16) | (x1 & 0xffff0000u);
-        out[1] = (x2 >> 16) | (x3 & 0xffff0000u);
+    for (int i = 0; i < QLOADS; ++i) {
+      const int cid = tid + 256 * i;
+      const int row = cid / KCH;
+      const int x = cid - row * KCH;
+      if (cid < BQ * KCH) {
+        *(u32x4*)(Qb + swz<DP>(row, 8 * x)) = qreg[i];
+        *(u32x4*)(Ob + swz<DP>(row, 8 * x)) = oreg[i];
       }
-      *(u32x2*)(&dstT[(8 * s_chunk + e) * TST + pos]) = out;
     }
-  };
-
-  auto store_q = [&]() {
-    if (tid < DP) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *(u32x4*)(&Qs[(4 * s_grp + i) * RST + 8 * s_chunk]) = qreg[i];
-        *(u32x4*)(&dOs[(4 * s_grp + i) * RST + 8 * s_chunk]) = oreg[i];
-      }
-      store_transposed(Qt, qreg);
-      store_transposed(dOt, oreg);
-    }
-    if (tid >= 256 - BQ) {
-      lse2s[tid - (256 - BQ)] = lse_r;
-      dds[tid - (256 - BQ)] = d_r;
+    if (st_lane >= 0) {
+      ((float*)(smem + OFF_LSE))[buf * BQ + st_lane] = lse_r;
+      ((float*)(smem + OFF_D))[buf * BQ + st_lane] = d_r;
     }
   };
 
@@ -284,38 +241,57 @@ __global__ __launch_bounds__(256) void thd_bwd_main_kernel(BwdParams p) {
     dv_acc[i] = f32x16{};
   }
 
-  __syncthreads();  // K staging fully consumed before the buffers are reused
-  if (n_iter > 0) load_q(0);
-  for (int iter = 0; iter < n_iter; ++iter) {
-    const int hq = hk * p.group + iter / n_qt;
-    const int q0 = q_start + (iter % n_qt) * BQ;
-    __syncthreads();
-    store_q();
-    __syncthreads();
-    if (iter + 1 < n_iter) load_q(iter + 1);
+  // Transpose-read addressing: lane s of a 16-lane group reads row
+  // R0 + s/4, columns C0 + 4*(s%4) .. +3.
+  const int tr_row = g16 >> 2;
+  const int tr_col = 4 * (g16 & 3);
 
-    const bool active = (kw0 < lk) && (!causal || q0 + BQ - 1 >= kw0);
-    if (active) {
+  const float c2 = p.c2;
+  const int dcol = 32 * w + r;  // d column of this lane in the dQ product
+  // (query head, first query row) of the current and of the next step
+  int hq = hk * p.group, q0 = q_start;
+  int hq_n = hq, q0_n = q0 + BQ;
+  if (q0_n >= lq) {
+    q0_n = q_start;
+    ++hq_n;
+  }
+  if (n_iter > 0) {
+    load_q(hq, q0);
+    store_q(0);
+  }
+  __syncthreads();
+  for (int iter = 0; iter < n_iter; ++iter) {
+    const int buf = iter & 1;
+    const bool more = iter + 1 < n_iter;
+    if (more) load_q(hq_n, q0_n);
+
+    const unsigned char* Qb = smem + OFF_Q + buf * TILE;
+    const unsigned char* Ob = smem + OFF_DO + buf * TILE;
+    const float* lse2s = (const float*)(smem + OFF_LSE) + buf * BQ;
+    const float* dds = (const float*)(smem + OFF_D) + buf * BQ;
+
+    // Every wave runs the products, also when none of its keys is visible to
+    // this query tile (then the mask zeroes P and dS): the accumulators are then
+    // updated unconditionally and stay in the MFMA registers across iterations.
+    {
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 a = *(const u32x4*)(&Qs[r * RST + 16 * c + 8 * h]);
+        const u32x4 a = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
         s = DT::mfma(as_vec8<DT>(a), kB[c], s);
       }
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 a = *(const u32x4*)(&dOs[r * RST + 16 * c + 8 * h]);
+        const u32x4 a = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
         dp = DT::mfma(as_vec8<DT>(a), vB[c], dp);
       }
-      const bool need_mask = (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);
+      const bool need_mask = (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);  // also when idle
+      const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], p.c2, -lse2s[qi]));
-        if (need_mask) {
-          const bool vis = (my_k < lk) && (!causal || my_k <= q0 + qi);
-          if (!vis) pv = 0.f;
-        }
+        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2s[qi]));
+        if (need_mask) pv = (my_k < lk && qi >= lim_lo) ? pv : 0.f;
         s[i] = pv;
         dp[i] = pv * (dp[i] - dds[qi]);
       }
@@ -331,15 +307,21 @@ __global__ __launch_bounds__(256) void thd_bwd_main_kernel(BwdParams p) {
         pb[kb] = pack8<DT>(tp);
         db[kb] = pack8<DT>(td);
       }
+      // dV^T += dO^T P and dK^T += Q^T dS.  A operand lane (r, h) needs
+      // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
+      // the order in which P / dS hold them: two transpose reads.
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+      for (int dt = 0; dt < ND; ++dt) {
+        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 ao = *(const u32x4*)(&dOt[(32 * dt + r) * TST + 16 * kb + 8 * h]);
+          const int r0 = 16 * kb + 4 * h + tr_row;
+          const u32x4 ao = cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
           dv_acc[dt] = DT::mfma(as_vec8<DT>(ao), pb[kb], dv_acc[dt]);
-          const u32x4 aq = *(const u32x4*)(&Qt[(32 * dt + r) * TST + 16 * kb + 8 * h]);
+          const u32x4 aq = cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
           dk_acc[dt] = DT::mfma(as_vec8<DT>(aq), db[kb], dk_acc[dt]);
         }
+      }
       // dS (query-major) for the workgroup-wide dQ product; elements are taken
       // from the packed 32-bit words (element j sits in word j/2, half j&1).
 #pragma unroll
@@ -353,61 +335,73 @@ __global__ __launch_bounds__(256) void thd_bwd_main_kernel(BwdParams p) {
         }
       }
     }
-    __syncthreads();
+    __syncthreads();  // dS complete; every wave is done with this query buffer
+    if (more) store_q(buf ^ 1);
 
     int kv_act = lk - k0;
     if (kv_act > BK) kv_act = BK;
     if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
-    if (w < ND && kv_act > 0) {
+    if (w < ND) {
+      // dQ[q][32w + r] = sum_kv dS[q][kv] K[kv][32w + r]; B operand lane
+      // (r, h) needs K rows 16kb + 8h + 0..7 at column 32w + r.
       const int nkb = (kv_act + 15) / 16;
+      const int c0 = 32 * w + 16 * (grp & 1) + tr_col;
       f32x16 dq = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < BK / 16; ++kb) {
         if (kb < nkb) {
           const u32x4 a = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
-          dq = DT::mfma(as_vec8<DT>(a), kA[kb], dq);
+          const int r0 = 16 * kb + 8 * h + tr_row;
+          const u32x4 kk = cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
+          dq = DT::mfma(as_vec8<DT>(a), as_vec8<DT>(kk), dq);
         }
       }
-      const int dcol = 32 * w + r;
-      if (dcol < p.d) {
-        float* base = p.dq_acc + (int64_t)hq * p.d + dcol;
+      // rows past lq fall outside the resource and are dropped
+      const rsrc_t acc_rs = make_rsrc(p.dq_acc + sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d,
+                                      (uint32_t)lq * accrow_bytes);
+      const uint32_t col = dcol < p.d ? 4u * dcol + (uint32_t)(q0 + 4 * h) * accrow_bytes
+                                      : kOobOffset;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = q0 + 8 * (i >> 2) + 4 * h + (i & 3);
-          const int64_t g = sq + qi;
-          if (qi < lq && g >= 0 && g < p.T_q) unsafeAtomicAdd(base + g * q_stride, dq[i]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t roff = (uint32_t)(8 * (i >> 2) + (i & 3)) * accrow_bytes;
+        buf_atomic_add(dq[i], acc_rs, col == kOobOffset ? kOobOffset : col + roff, 0);
       }
+    }
+    __syncthreads();  // next query buffer visible; dS reads done
+    hq = hq_n;
+    q0 = q0_n;
+    q0_n += BQ;
+    if (q0_n >= lq) {
+      q0_n = q_start;
+      ++hq_n;
     }
   }
 
-  // Epilogue: this lane's key row of dK (scaled) and dV.
-  if (my_k < lk) {
-    const int64_t g = sk + my_k;
-    if (g >= 0 && g < p.T_kv) {
-      uint16_t* dkp = p.dk + g * kv_stride + (int64_t)hk * p.d;
-      uint16_t* dvp = p.dv + g * kv_stride + (int64_t)hk * p.d;
+  // Epilogue: this lane's key row of dK (scaled) and dV; rows past lk dropped.
+  const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
+                                 kv_bytes);
+  const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
+                                 kv_bytes);
+  const uint32_t krow = (uint32_t)(32 * w + r) * kvrow_bytes;
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+  for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int dd = 32 * dt + 8 * gq + 4 * h;
-          if (dd < p.d) {
-            u32x2 ok, ov;
-            ok[0] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 0] * p.scale) |
-                    ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 1] * p.scale) << 16);
-            ok[1] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 2] * p.scale) |
-                    ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 3] * p.scale) << 16);
-            ov[0] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 0]) |
-                    ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 1]) << 16);
-            ov[1] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 2]) |
-                    ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 3]) << 16);
-            *(u32x2*)(dkp + dd) = ok;
-            *(u32x2*)(dvp + dd) = ov;
-          }
-        }
+    for (int gq = 0; gq < 4; ++gq) {
+      const int dd = 32 * dt + 8 * gq + 4 * h;
+      if (dd < p.d) {
+        u32x2 ok, ov;
+        ok[0] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 0] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 1] * p.scale) << 16);
+        ok[1] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 2] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 3] * p.scale) << 16);
+        ov[0] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 0]) |
+                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 1]) << 16);
+        ov[1] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 2]) |
+                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 3]) << 16);
+        buf_store8(ok, dk_rs, krow + 2u * dd, 0);
+        buf_store8(ov, dv_rs, krow + 2u * dd, 0);
+      }
     }
-  }
 }
 
 // ---------------------------------------------------------------------------

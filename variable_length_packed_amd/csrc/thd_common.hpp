@@ -118,6 +118,40 @@ __device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff,
   __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)voff, (int)soff, 0);
 }
 
+// ---------------------------------------------------------------------------
+// LDS tiles.  A [rows][DP] tile of 16-bit elements is stored row-major with
+// its 16-byte chunks XOR-swizzled per row, so that 8 consecutive rows read at
+// the same logical chunk (MFMA operand rows) and 4 consecutive rows read at
+// two neighbouring chunks (transpose reads) fall in distinct bank groups.
+// ---------------------------------------------------------------------------
+template <int DP>
+__device__ __forceinline__ uint32_t swz(int row, int elem) {
+  constexpr int KCH = DP / 8;
+  const int f = (2 * (row & 3) + ((row >> 2) & 1)) & (KCH - 1);
+  return (uint32_t)row * (DP * 2) + ((uint32_t)((elem >> 3) ^ f) << 4) + (uint32_t)(elem & 7) * 2;
+}
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i%4 of the 8-byte rows addressed by lanes i/4, i/4+4, i/4+8, i/4+12 of the
+// group (in that order).  With lane s addressing row R0 + s/4 at column
+// C0 + 4*(s%4), lane i gets column C0 + i of rows R0 .. R0+3.
+__device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* lds, uint32_t byte_off) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + byte_off));
+  return __builtin_bit_cast(u32x2, v);
+}
+
+__device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) {
+  u32x4 r;
+  r[0] = a[0];
+  r[1] = a[1];
+  r[2] = b[0];
+  r[3] = b[1];
+  return r;
+}
+
 // Rows of a sequence that may be touched: [start, start + n) intersected with
 // [0, T), and few enough that n * row_bytes stays below 2^31.
 __device__ __forceinline__ int clamp_rows(int64_t start, int len, int64_t T, int64_t row_bytes) {
