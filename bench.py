@@ -41,6 +41,32 @@ def parse():
     return ap.parse_args()
 
 
+def source_digest():
+    """Digest of the HIP sources; counter-based traffic is valid only for them."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for path in sorted(glob.glob(os.path.join(ROOT, "variable_length_packed_amd", "csrc", "*"))):
+        h.update(os.path.basename(path).encode())
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload_tag):
+    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE record
+    of this kernel and workload, or None when the kernel has changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest():
+        return None
+    return int(rec["bytes_per_launch"])
+
+
 def copy_calibration(mib):
     """A plain copy kernel of known size: reads and writes exactly mib MiB."""
     import torch
@@ -186,7 +212,8 @@ def main():
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
     roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": (measured_traffic(dom, "16seq_causal_h16_d128") if w.name == "2" else None),
                 "avg_launch_ms": round(dom_ms, 4)}
 
     out = {

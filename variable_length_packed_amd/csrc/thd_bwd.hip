@@ -19,6 +19,8 @@
 //          takes d columns 32w..32w+31) and added to the accumulator with
 //          fp32 atomics;
 //   post : dQ accumulator -> storage dtype, zeros on pad rows of dK and dV.
+#include <type_traits>
+
 #include "thd_common.hpp"
 #include "thd_launch.hpp"
 
@@ -57,7 +59,7 @@ struct BwdParams {
 // ---------------------------------------------------------------------------
 // pre: D = rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
 // ---------------------------------------------------------------------------
-template <class DT>
+template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
@@ -77,9 +79,13 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
         acc += DT::to_f32((uint16_t)(a[w] >> 16)) * DT::to_f32((uint16_t)(g[w] >> 16));
       }
     }
+  }
+  if (8 * c < DP) {
+    // accumulator layout [h_q][T_q][DP]
+    float* acc = p.dq_acc + ((int64_t)hh * p.T_q + row) * DP + 8 * c;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)(p.dq_acc + off) = z;
-    *(f32x4*)(p.dq_acc + off + 4) = z;
+    *(f32x4*)acc = z;
+    *(f32x4*)(acc + 4) = z;
   }
   acc += __shfl_xor(acc, 8, 16);
   acc += __shfl_xor(acc, 4, 16);
@@ -104,7 +110,8 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int SST = BK + 8;   // dS row stride (elements)
   constexpr int TILE = BQ * DP * 2;
   constexpr int OFF_K = 0;
-  constexpr int OFF_Q = OFF_K + BK * DP * 2;
+  constexpr int OFF_V = OFF_K + BK * DP * 2;
+  constexpr int OFF_Q = OFF_V + BK * DP * 2;
   constexpr int OFF_DO = OFF_Q + 2 * TILE;
   constexpr int OFF_LSE = OFF_DO + 2 * TILE;
   constexpr int OFF_D = OFF_LSE + 2 * BQ * 4;
@@ -112,6 +119,7 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int SMEM = OFF_DS + BQ * SST * 2;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   unsigned char* Kt = smem + OFF_K;
+  unsigned char* Vt = smem + OFF_V;
   uint16_t* dSs = (uint16_t*)(smem + OFF_DS);
 
   const int bid = blockIdx.x;
@@ -124,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   tile_in_seq = uniform(tile_in_seq);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);
   const int l = tid & 63;
   const int r = l & 31;
   const int h = l >> 5;
@@ -151,7 +159,9 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
   const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
 
-  // K tile -> LDS (row-major, swizzled).
+  // K and V tiles -> LDS (row-major, swizzled).  The B operands of
+  // S = Q K^T and dP = dO V^T (lane: key 32w + r, d chunk 16c + 8h) are read
+  // from there every step, which keeps registers free for operand prefetch.
 #pragma unroll
   for (int i = 0; i < BK * KCH / 256; ++i) {
     const int cid = tid + 256 * i;
@@ -159,21 +169,9 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
     const int x = cid - row * KCH;
     const uint32_t off = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
     *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, off, 0);
-  }
-  // V of this lane's key as the B operand of dP = dO V^T.
-  typename DT::vec8 vB[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int dd = 16 * c + 8 * h;
-    const uint32_t off = dd < p.d ? (uint32_t)(32 * w + r) * kvrow_bytes + 2u * dd : kOobOffset;
-    vB[c] = as_vec8<DT>(buf_load16(v_rs, off, 0));
+    *(u32x4*)(Vt + swz<DP>(row, 8 * x)) = buf_load16(v_rs, off, 0);
   }
   __syncthreads();
-  // K of this lane's key as the B operand of S = Q K^T (from the LDS tile).
-  typename DT::vec8 kB[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c)
-    kB[c] = as_vec8<DT>(*(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h)));
 
   // Query tiles: from the first tile that can see key k0 when causal.
   const int q_start = causal ? (k0 / BQ) * BQ : 0;
@@ -274,17 +272,37 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
     // this query tile (then the mask zeroes P and dS): the accumulators are then
     // updated unconditionally and stay in the MFMA registers across iterations.
     {
+      // Operands of S = Q K^T and dP = dO V^T, all read before the products so
+      // that LDS latency overlaps; the two independent chains are interleaved.
+      u32x4 qa[NC], ka[NC], oa[NC], va[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        qa[c] = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
+        ka[c] = *(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h));
+        oa[c] = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
+        va[c] = *(const u32x4*)(Vt + swz<DP>(32 * w + r, 16 * c + 8 * h));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 a = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
-        s = DT::mfma(as_vec8<DT>(a), kB[c], s);
+        s = DT::mfma(as_vec8<DT>(qa[c]), as_vec8<DT>(ka[c]), s);
+        dp = DT::mfma(as_vec8<DT>(oa[c]), as_vec8<DT>(va[c]), dp);
       }
+      // Transposed operands of dV^T += dO^T P and dK^T += Q^T dS (see below),
+      // read while the softmax arithmetic runs.
+      u32x4 to[ND][2], tq[ND][2];
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const u32x4 a = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
-        dp = DT::mfma(as_vec8<DT>(a), vB[c], dp);
+      for (int dt = 0; dt < ND; ++dt) {
+        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int r0 = 16 * kb + 4 * h + tr_row;
+          to[dt][kb] = cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
+          tq[dt][kb] = cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
+        }
       }
+      __builtin_amdgcn_sched_barrier(0);
       const bool need_mask = (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);  // also when idle
       const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
 #pragma unroll
@@ -311,17 +329,12 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
       // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
       // the order in which P / dS hold them: two transpose reads.
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int r0 = 16 * kb + 4 * h + tr_row;
-          const u32x4 ao = cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
-          dv_acc[dt] = DT::mfma(as_vec8<DT>(ao), pb[kb], dv_acc[dt]);
-          const u32x4 aq = cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
-          dk_acc[dt] = DT::mfma(as_vec8<DT>(aq), db[kb], dk_acc[dt]);
+          dv_acc[dt] = DT::mfma(as_vec8<DT>(to[dt][kb]), pb[kb], dv_acc[dt]);
+          dk_acc[dt] = DT::mfma(as_vec8<DT>(tq[dt][kb]), db[kb], dk_acc[dt]);
         }
-      }
       // dS (query-major) for the workgroup-wide dQ product; elements are taken
       // from the packed 32-bit words (element j sits in word j/2, half j&1).
 #pragma unroll
@@ -346,25 +359,32 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
       // (r, h) needs K rows 16kb + 8h + 0..7 at column 32w + r.
       const int nkb = (kv_act + 15) / 16;
       const int c0 = 32 * w + 16 * (grp & 1) + tr_col;
-      f32x16 dq = f32x16{};
+      u32x4 da[BK / 16], kt[BK / 16];
 #pragma unroll
       for (int kb = 0; kb < BK / 16; ++kb) {
         if (kb < nkb) {
-          const u32x4 a = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
+          da[kb] = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
           const int r0 = 16 * kb + 8 * h + tr_row;
-          const u32x4 kk = cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
-          dq = DT::mfma(as_vec8<DT>(a), as_vec8<DT>(kk), dq);
+          kt[kb] = cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
         }
       }
-      // rows past lq fall outside the resource and are dropped
-      const rsrc_t acc_rs = make_rsrc(p.dq_acc + sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d,
-                                      (uint32_t)lq * accrow_bytes);
-      const uint32_t col = dcol < p.d ? 4u * dcol + (uint32_t)(q0 + 4 * h) * accrow_bytes
-                                      : kOobOffset;
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16 dq = f32x16{};
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t roff = (uint32_t)(8 * (i >> 2) + (i & 3)) * accrow_bytes;
-        buf_atomic_add(dq[i], acc_rs, col == kOobOffset ? kOobOffset : col + roff, 0);
+      for (int kb = 0; kb < BK / 16; ++kb)
+        if (kb < nkb) dq = DT::mfma(as_vec8<DT>(da[kb]), as_vec8<DT>(kt[kb]), dq);
+      // rows past lq fall outside the resource and are dropped; accumulator
+      // layout [h_q][T_q][DP], so the 4 rows of a group are immediate offsets
+      const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq * p.T_q + sq) * DP,
+                                      (uint32_t)lq * (DP * 4));
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t base =
+            dcol < p.d ? (uint32_t)((q0 + 8 * g + 4 * h) * DP + dcol) * 4u : kOobOffset;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          buf_atomic_add(dq[4 * g + e], acc_rs,
+                         base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
       }
     }
     __syncthreads();  // next query buffer visible; dS reads done
@@ -407,21 +427,29 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // post: dq = scale * dq_acc in the storage dtype; zero pad rows of dk / dv.
 // ---------------------------------------------------------------------------
-template <class DT>
+template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int64_t n_chunks,
                                                            int n_conv_wg) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_conv_wg) {
+    // chunk idx = ((hq * T_q) + row) * (d/8) + c: reads the head-major
+    // accumulator in order, writes dq[row][hq][8c .. 8c+7]
     const int64_t idx = (int64_t)blockIdx.x * 256 + tid;
     if (idx >= n_chunks) return;
-    const f32x4 a = *(const f32x4*)(p.dq_acc + 8 * idx);
-    const f32x4 c = *(const f32x4*)(p.dq_acc + 8 * idx + 4);
+    const int cpr = p.d / 8;
+    const int64_t hr = idx / cpr;
+    const int c8 = (int)(idx - hr * cpr) * 8;
+    const int64_t hq = hr / p.T_q;
+    const int64_t row = hr - hq * p.T_q;
+    const float* src = p.dq_acc + hr * DP + c8;
+    const f32x4 a = *(const f32x4*)src;
+    const f32x4 c = *(const f32x4*)(src + 4);
     u32x4 out;
     out[0] = (uint32_t)DT::bits(a[0] * p.scale) | ((uint32_t)DT::bits(a[1] * p.scale) << 16);
     out[1] = (uint32_t)DT::bits(a[2] * p.scale) | ((uint32_t)DT::bits(a[3] * p.scale) << 16);
     out[2] = (uint32_t)DT::bits(c[0] * p.scale) | ((uint32_t)DT::bits(c[1] * p.scale) << 16);
     out[3] = (uint32_t)DT::bits(c[2] * p.scale) | ((uint32_t)DT::bits(c[3] * p.scale) << 16);
-    *(u32x4*)(p.dq + 8 * idx) = out;
+    *(u32x4*)(p.dq + (row * p.h_q + hq) * p.d + c8) = out;
     return;
   }
   __shared__ uint8_t invalid[kZeroRowsB];
@@ -456,7 +484,7 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   if (em != hipSuccess) return em;
   const int64_t pairs = bp.T_q * bp.h_q;
   if (pairs > 0) {
-    hipLaunchKernelGGL((thd_bwd_pre_kernel<DT>), dim3((unsigned)((pairs + 15) / 16)), dim3(256),
+    hipLaunchKernelGGL((thd_bwd_pre_kernel<DT, DP>), dim3((unsigned)((pairs + 15) / 16)), dim3(256),
                        0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -472,7 +500,7 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   const int64_t n_conv = (n_chunks + 255) / 256;
   const int64_t n_zero = (bp.T_kv + kZeroRowsB - 1) / kZeroRowsB;
   if (n_conv + n_zero > 0) {
-    hipLaunchKernelGGL((thd_bwd_post_kernel<DT>), dim3((unsigned)(n_conv + n_zero)), dim3(256), 0,
+    hipLaunchKernelGGL((thd_bwd_post_kernel<DT, DP>), dim3((unsigned)(n_conv + n_zero)), dim3(256), 0,
                        s, bp, n_chunks, (int)n_conv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -482,10 +510,14 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+int padded_dim(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : 128; }
+
 }  // namespace
 
+// fp32 dq accumulator [h_q][T_q][DP] (DP = head_dim rounded up to 32, 64 or
+// 128) followed by D = rowsum(dO * O) [h_q][T_q].
 size_t bwd_workspace_bytes(const Problem& p) {
-  const size_t acc = align256((size_t)p.T_q * p.h_q * p.d * sizeof(float));
+  const size_t acc = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
   const size_t dsum = align256((size_t)p.T_q * p.h_q * sizeof(float));
   return acc + dsum;
 }
@@ -504,7 +536,8 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   bp.dk = (uint16_t*)dk;
   bp.dv = (uint16_t*)dv;
   bp.dq_acc = (float*)workspace;
-  bp.dsum = (float*)((char*)workspace + align256((size_t)p.T_q * p.h_q * p.d * sizeof(float)));
+  bp.dsum = (float*)((char*)workspace +
+                     align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float)));
   bp.cu_q = p.cu_q;
   bp.cu_kv = p.cu_kv;
   bp.pad_q = p.pad_q;

@@ -120,14 +120,19 @@ __device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff,
 
 // ---------------------------------------------------------------------------
 // LDS tiles.  A [rows][DP] tile of 16-bit elements is stored row-major with
-// its 16-byte chunks XOR-swizzled per row, so that 8 consecutive rows read at
-// the same logical chunk (MFMA operand rows) and 4 consecutive rows read at
-// two neighbouring chunks (transpose reads) fall in distinct bank groups.
+// its 16-byte chunks XOR-swizzled per row by f(row).  For DP = 128, f is a
+// bijection on 16 consecutive rows (MFMA operand rows read at one logical
+// chunk hit 16 distinct 16-byte bank groups), its bits 1-2 and bits 2-3 are
+// each distinct on 4 consecutive rows starting at a multiple of 4 (transpose
+// reads of 4 rows x 2 or 4 neighbouring chunks), and its bits 0-2 are a
+// bijection on 8 consecutive rows -- conflict-free for both a 32- and a
+// 64-bank view of LDS.
 // ---------------------------------------------------------------------------
 template <int DP>
 __device__ __forceinline__ uint32_t swz(int row, int elem) {
   constexpr int KCH = DP / 8;
-  const int f = (2 * (row & 3) + ((row >> 2) & 1)) & (KCH - 1);
+  const int f = (((0xAC60 >> (4 * (row & 3))) & 15) ^ ((row >> 2) & 1) ^ (((row >> 3) & 1) << 3)) &
+                (KCH - 1);
   return (uint32_t)row * (DP * 2) + ((uint32_t)((elem >> 3) ^ f) << 4) + (uint32_t)(elem & 7) * 2;
 }
 
