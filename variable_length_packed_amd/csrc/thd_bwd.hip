@@ -97,12 +97,20 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 // main
 // ---------------------------------------------------------------------------
-// LDS: the K tile [BK][DP] (resident), two buffers of the query tile (Q and
-// dO [BQ][DP], LSE and D [BQ]) and dS [BQ][BK] (padded rows).  Q, dO and K
-// are stored row-major (swizzled); their transposes for dV^T = dO^T P,
-// dK^T = Q^T dS and dQ = dS K come from transpose reads.
+// One workgroup of 8 waves per (sequence, 128-key tile, kv head).  The waves
+// form two halves of 4; wave w of a half owns keys 32w .. 32w+31 and keeps
+// dK^T / dV^T for them in registers.  The halves share the K and V tiles in
+// LDS and take alternate query tiles (items 2j + half of the list
+// "every query head of the GQA group x every 32-row query tile from the
+// diagonal"), each with its own double-buffered Q / dO / LSE / D tiles and dS
+// tile, so two waves share each SIMD.  At the end the halves' dK and dV are
+// summed through LDS.
+//
+// LDS (bytes, DP = 128): K 32K, V 32K, per half 2 x (Q 8K + dO 8K) + LSE/D
+// 512 + dS 8.5K.  Q, dO, K and V are row-major with swizzled 16-byte chunks;
+// Q^T, dO^T and K^T operands come from transpose reads.
 template <class DT, int DP>
-__global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
+__global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int BK = kBwdBK, BQ = kBwdBQ;
   constexpr int NC = DP / 16;
   constexpr int ND = DP / 32;
@@ -111,16 +119,19 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int TILE = BQ * DP * 2;
   constexpr int OFF_K = 0;
   constexpr int OFF_V = OFF_K + BK * DP * 2;
-  constexpr int OFF_Q = OFF_V + BK * DP * 2;
-  constexpr int OFF_DO = OFF_Q + 2 * TILE;
-  constexpr int OFF_LSE = OFF_DO + 2 * TILE;
-  constexpr int OFF_D = OFF_LSE + 2 * BQ * 4;
-  constexpr int OFF_DS = OFF_D + 2 * BQ * 4;
-  constexpr int SMEM = OFF_DS + BQ * SST * 2;
+  constexpr int OFF_HALF = OFF_V + BK * DP * 2;
+  // half-local layout
+  constexpr int H_Q = 0;
+  constexpr int H_DO = H_Q + 2 * TILE;
+  constexpr int H_LSE = H_DO + 2 * TILE;
+  constexpr int H_D = H_LSE + 2 * BQ * 4;
+  constexpr int H_DS = H_D + 2 * BQ * 4;
+  constexpr int HALF_BYTES = H_DS + BQ * SST * 2;
+  constexpr int SMEM = OFF_HALF + 2 * HALF_BYTES;
+  static_assert(2 * 4 * 64 * ND * 16 * 4 <= SMEM, "dK/dV reduction must fit the LDS");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   unsigned char* Kt = smem + OFF_K;
   unsigned char* Vt = smem + OFF_V;
-  uint16_t* dSs = (uint16_t*)(smem + OFF_DS);
 
   const int bid = blockIdx.x;
   const int logical = xcd_remap(bid, p.n_main);
@@ -132,12 +143,17 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   tile_in_seq = uniform(tile_in_seq);
 
   const int tid = threadIdx.x;
-  const int w = uniform(tid >> 6);
+  const int wg = uniform(tid >> 6);  // wave in the workgroup, 0..7
+  const int half = wg >> 2;
+  const int w = wg & 3;              // wave in its half: keys 32w .. 32w+31
+  const int ltid = tid & 255;        // thread in its half
   const int l = tid & 63;
   const int r = l & 31;
   const int h = l >> 5;
-  const int g16 = l & 15;        // lane inside its 16-lane group
-  const int grp = l >> 4;        // 16-lane group of the wave
+  const int g16 = l & 15;            // lane inside its 16-lane group
+  const int grp = l >> 4;            // 16-lane group of the wave
+  unsigned char* hbase = smem + OFF_HALF + half * HALF_BYTES;
+  uint16_t* dSs = (uint16_t*)(hbase + H_DS);
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
@@ -156,32 +172,30 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
-  const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
-  const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
-
-  // K and V tiles -> LDS (row-major, swizzled).  The B operands of
-  // S = Q K^T and dP = dO V^T (lane: key 32w + r, d chunk 16c + 8h) are read
-  // from there every step, which keeps registers free for operand prefetch.
+  {
+    const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
+    const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
 #pragma unroll
-  for (int i = 0; i < BK * KCH / 256; ++i) {
-    const int cid = tid + 256 * i;
-    const int row = cid / KCH;
-    const int x = cid - row * KCH;
-    const uint32_t off = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
-    *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, off, 0);
-    *(u32x4*)(Vt + swz<DP>(row, 8 * x)) = buf_load16(v_rs, off, 0);
+    for (int i = 0; i < BK * KCH / 512; ++i) {
+      const int cid = tid + 512 * i;
+      const int row = cid / KCH;
+      const int x = cid - row * KCH;
+      const uint32_t off = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
+      *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, off, 0);
+      *(u32x4*)(Vt + swz<DP>(row, 8 * x)) = buf_load16(v_rs, off, 0);
+    }
   }
-  __syncthreads();
 
   // Query tiles: from the first tile that can see key k0 when causal.
   const int q_start = causal ? (k0 / BQ) * BQ : 0;
   const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
   const int n_iter = p.group * n_qt;
+  const int n_rounds = (n_iter + 1) / 2;
 
-  // Staging of one query tile: BQ*KCH chunks of Q and of dO; threads
-  // 256-BQ .. 255 also fetch LSE and D.
+  // Staging of one query tile by the 256 threads of a half: BQ*KCH chunks of
+  // Q and of dO; threads 256-BQ .. 255 of the half also fetch LSE and D.
   constexpr int QLOADS = (BQ * KCH + 255) / 256;
-  const int st_lane = tid - (256 - BQ);
+  const int st_lane = ltid - (256 - BQ);
   u32x4 qreg[QLOADS], oreg[QLOADS];
   float lse_r = 0.f, d_r = 0.f;
 
@@ -191,7 +205,7 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
     const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
 #pragma unroll
     for (int i = 0; i < QLOADS; ++i) {
-      const int cid = tid + 256 * i;
+      const int cid = ltid + 256 * i;
       const int row = cid / KCH;
       const int x = cid - row * KCH;
       const uint32_t off = (cid < BQ * KCH && 8 * x < p.d)
@@ -214,11 +228,11 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   };
 
   auto store_q = [&](int buf) {
-    unsigned char* Qb = smem + OFF_Q + buf * TILE;
-    unsigned char* Ob = smem + OFF_DO + buf * TILE;
+    unsigned char* Qb = hbase + H_Q + buf * TILE;
+    unsigned char* Ob = hbase + H_DO + buf * TILE;
 #pragma unroll
     for (int i = 0; i < QLOADS; ++i) {
-      const int cid = tid + 256 * i;
+      const int cid = ltid + 256 * i;
       const int row = cid / KCH;
       const int x = cid - row * KCH;
       if (cid < BQ * KCH) {
@@ -227,10 +241,15 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
       }
     }
     if (st_lane >= 0) {
-      ((float*)(smem + OFF_LSE))[buf * BQ + st_lane] = lse_r;
-      ((float*)(smem + OFF_D))[buf * BQ + st_lane] = d_r;
+      ((float*)(hbase + H_LSE))[buf * BQ + st_lane] = lse_r;
+      ((float*)(hbase + H_D))[buf * BQ + st_lane] = d_r;
     }
   };
+
+  // A half without an item (last round, odd count) still runs the products
+  // on its buffers with everything masked: start them as finite zeros.
+  for (int i = ltid; i < (2 * TILE * 2 + 4 * BQ * 4) / 16; i += 256)
+    ((u32x4*)hbase)[i] = u32x4{0u, 0u, 0u, 0u};
 
   f32x16 dk_acc[ND], dv_acc[ND];
 #pragma unroll
@@ -243,73 +262,62 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
   // R0 + s/4, columns C0 + 4*(s%4) .. +3.
   const int tr_row = g16 >> 2;
   const int tr_col = 4 * (g16 & 3);
-
   const float c2 = p.c2;
   const int dcol = 32 * w + r;  // d column of this lane in the dQ product
-  // (query head, first query row) of the current and of the next step
-  int hq = hk * p.group, q0 = q_start;
-  int hq_n = hq, q0_n = q0 + BQ;
-  if (q0_n >= lq) {
-    q0_n = q_start;
-    ++hq_n;
-  }
-  if (n_iter > 0) {
+
+  // Item it -> (query head, first query row); a half walks it = half, +2, ...
+  auto item = [&](int it, int& hq_, int& q0_) {
+    const int hi = it / n_qt;
+    hq_ = hk * p.group + hi;
+    q0_ = q_start + (it - hi * n_qt) * BQ;
+  };
+  int it = half;
+  int hq = 0, q0 = 0;
+  if (it < n_iter) item(it, hq, q0);
+  __syncthreads();  // K / V tiles and zeroed buffers visible
+  if (it < n_iter) {
     load_q(hq, q0);
     store_q(0);
   }
   __syncthreads();
-  for (int iter = 0; iter < n_iter; ++iter) {
-    const int buf = iter & 1;
-    const bool more = iter + 1 < n_iter;
-    if (more) load_q(hq_n, q0_n);
+  for (int round = 0; round < n_rounds; ++round, it += 2) {
+    const int buf = round & 1;
+    const bool live = it < n_iter;
+    const bool more = it + 2 < n_iter;
+    int hq_n = 0, q0_n = 0;
+    if (more) {
+      item(it + 2, hq_n, q0_n);
+      load_q(hq_n, q0_n);
+    }
 
-    const unsigned char* Qb = smem + OFF_Q + buf * TILE;
-    const unsigned char* Ob = smem + OFF_DO + buf * TILE;
-    const float* lse2s = (const float*)(smem + OFF_LSE) + buf * BQ;
-    const float* dds = (const float*)(smem + OFF_D) + buf * BQ;
+    const unsigned char* Qb = hbase + H_Q + buf * TILE;
+    const unsigned char* Ob = hbase + H_DO + buf * TILE;
+    const float* lse2s = (const float*)(hbase + H_LSE) + buf * BQ;
+    const float* dds = (const float*)(hbase + H_D) + buf * BQ;
 
     // Every wave runs the products, also when none of its keys is visible to
-    // this query tile (then the mask zeroes P and dS): the accumulators are then
-    // updated unconditionally and stay in the MFMA registers across iterations.
+    // this query tile or its half has no item (then the mask zeroes P and
+    // dS): the accumulators are updated unconditionally and stay in the MFMA
+    // registers across iterations.
     {
-      // Operands of S = Q K^T and dP = dO V^T, all read before the products so
-      // that LDS latency overlaps; the two independent chains are interleaved.
-      u32x4 qa[NC], ka[NC], oa[NC], va[NC];
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        qa[c] = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
-        ka[c] = *(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h));
-        oa[c] = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
-        va[c] = *(const u32x4*)(Vt + swz<DP>(32 * w + r, 16 * c + 8 * h));
-      }
-      __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the products
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        s = DT::mfma(as_vec8<DT>(qa[c]), as_vec8<DT>(ka[c]), s);
-        dp = DT::mfma(as_vec8<DT>(oa[c]), as_vec8<DT>(va[c]), dp);
+        const u32x4 qa = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
+        const u32x4 ka = *(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h));
+        const u32x4 oa = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
+        const u32x4 va = *(const u32x4*)(Vt + swz<DP>(32 * w + r, 16 * c + 8 * h));
+        s = DT::mfma(as_vec8<DT>(qa), as_vec8<DT>(ka), s);
+        dp = DT::mfma(as_vec8<DT>(oa), as_vec8<DT>(va), dp);
       }
-      // Transposed operands of dV^T += dO^T P and dK^T += Q^T dS (see below),
-      // read while the softmax arithmetic runs.
-      u32x4 to[ND][2], tq[ND][2];
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int r0 = 16 * kb + 4 * h + tr_row;
-          to[dt][kb] = cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
-          tq[dt][kb] = cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      const bool need_mask = (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);  // also when idle
+      const bool need_mask = !live || (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);
       const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
+      const bool key_ok = live && my_k < lk;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
         float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2s[qi]));
-        if (need_mask) pv = (my_k < lk && qi >= lim_lo) ? pv : 0.f;
+        if (need_mask) pv = (key_ok && qi >= lim_lo) ? pv : 0.f;
         s[i] = pv;
         dp[i] = pv * (dp[i] - dds[qi]);
       }
@@ -329,13 +337,20 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
       // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
       // the order in which P / dS hold them: two transpose reads.
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
+      for (int dt = 0; dt < ND; ++dt) {
+        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          dv_acc[dt] = DT::mfma(as_vec8<DT>(to[dt][kb]), pb[kb], dv_acc[dt]);
-          dk_acc[dt] = DT::mfma(as_vec8<DT>(tq[dt][kb]), db[kb], dk_acc[dt]);
+          const int r0 = 16 * kb + 4 * h + tr_row;
+          const u32x4 to =
+              cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
+          const u32x4 tq =
+              cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
+          dv_acc[dt] = DT::mfma(as_vec8<DT>(to), pb[kb], dv_acc[dt]);
+          dk_acc[dt] = DT::mfma(as_vec8<DT>(tq), db[kb], dk_acc[dt]);
         }
-      // dS (query-major) for the workgroup-wide dQ product; elements are taken
+      }
+      // dS (query-major) for the dQ product of this half; elements are taken
       // from the packed 32-bit words (element j sits in word j/2, half j&1).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -351,28 +366,25 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
     __syncthreads();  // dS complete; every wave is done with this query buffer
     if (more) store_q(buf ^ 1);
 
-    int kv_act = lk - k0;
-    if (kv_act > BK) kv_act = BK;
-    if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
-    if (w < ND) {
+    if (live && w < ND) {
       // dQ[q][32w + r] = sum_kv dS[q][kv] K[kv][32w + r]; B operand lane
       // (r, h) needs K rows 16kb + 8h + 0..7 at column 32w + r.
+      int kv_act = lk - k0;
+      if (kv_act > BK) kv_act = BK;
+      if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
       const int nkb = (kv_act + 15) / 16;
       const int c0 = 32 * w + 16 * (grp & 1) + tr_col;
-      u32x4 da[BK / 16], kt[BK / 16];
+      f32x16 dq = f32x16{};
 #pragma unroll
       for (int kb = 0; kb < BK / 16; ++kb) {
         if (kb < nkb) {
-          da[kb] = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
+          const u32x4 da = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
           const int r0 = 16 * kb + 8 * h + tr_row;
-          kt[kb] = cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
+          const u32x4 kt =
+              cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
+          dq = DT::mfma(as_vec8<DT>(da), as_vec8<DT>(kt), dq);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x16 dq = f32x16{};
-#pragma unroll
-      for (int kb = 0; kb < BK / 16; ++kb)
-        if (kb < nkb) dq = DT::mfma(as_vec8<DT>(da[kb]), as_vec8<DT>(kt[kb]), dq);
       // rows past lq fall outside the resource and are dropped; accumulator
       // layout [h_q][T_q][DP], so the 4 rows of a group are immediate offsets
       const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq * p.T_q + sq) * DP,
@@ -387,21 +399,36 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
                          base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
       }
     }
-    __syncthreads();  // next query buffer visible; dS reads done
+    __syncthreads();  // next query buffers visible; dS reads done
     hq = hq_n;
     q0 = q0_n;
-    q0_n += BQ;
-    if (q0_n >= lq) {
-      q0_n = q_start;
-      ++hq_n;
-    }
   }
 
-  // Epilogue: this lane's key row of dK (scaled) and dV; rows past lk dropped.
-  const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
-  const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
+  // Sum the halves: half 1 parks its dK, half 0 its dV in LDS (element-major,
+  // lane-contiguous), then half 0 writes dK and half 1 writes dV.
+  float* red = (float*)smem;
+  constexpr int PER = 4 * 64;  // lanes of one half
+  const int slot = w * 64 + l;
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float x = half ? dk_acc[dt][i] : dv_acc[dt][i];
+      red[(half * ND * 16 + dt * 16 + i) * PER + slot] = x;
+    }
+  __syncthreads();
+  f32x16 out[ND];
+#pragma unroll
+  for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float other = red[((1 - half) * ND * 16 + dt * 16 + i) * PER + slot];
+      out[dt][i] = (half ? dv_acc[dt][i] : dk_acc[dt][i]) + other;
+    }
+  const float mul = half ? 1.f : p.scale;  // dK carries the softmax scale
+  uint16_t* dst = half ? p.dv : p.dk;
+  const rsrc_t o_rs = make_rsrc(dst + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
+                                kv_bytes);
   const uint32_t krow = (uint32_t)(32 * w + r) * kvrow_bytes;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
@@ -409,17 +436,12 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_kernel(BwdParams p) {
     for (int gq = 0; gq < 4; ++gq) {
       const int dd = 32 * dt + 8 * gq + 4 * h;
       if (dd < p.d) {
-        u32x2 ok, ov;
-        ok[0] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 0] * p.scale) |
-                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 1] * p.scale) << 16);
-        ok[1] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 2] * p.scale) |
-                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 3] * p.scale) << 16);
-        ov[0] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 0]) |
-                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 1]) << 16);
-        ov[1] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 2]) |
-                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 3]) << 16);
-        buf_store8(ok, dk_rs, krow + 2u * dd, 0);
-        buf_store8(ov, dv_rs, krow + 2u * dd, 0);
+        u32x2 ov;
+        ov[0] = (uint32_t)DT::bits(out[dt][4 * gq + 0] * mul) |
+                ((uint32_t)DT::bits(out[dt][4 * gq + 1] * mul) << 16);
+        ov[1] = (uint32_t)DT::bits(out[dt][4 * gq + 2] * mul) |
+                ((uint32_t)DT::bits(out[dt][4 * gq + 3] * mul) << 16);
+        buf_store8(ov, o_rs, krow + 2u * dd, 0);
       }
     }
 }
@@ -491,7 +513,7 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   }
   if ((em = mark(1)) != hipSuccess) return em;
   if (bp.n_main > 0) {
-    hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(256), 0, s, bp);
+    hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(512), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
