@@ -10,13 +10,15 @@
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
 // Three launches:
-//   pre  : D per (row, head) and zeroing of the fp32 dQ accumulator;
-//   main : one workgroup per (sequence, 128-key tile, kv head); each wave
-//          owns 32 keys and keeps K, V, dK^T and dV^T in registers while it
-//          walks the 32-row query tiles (from the diagonal when causal) of
-//          every query head of its GQA group.  dQ of a query tile is
-//          computed by the whole workgroup from dS staged in LDS (wave w
-//          takes d columns 32w..32w+31) and added to the accumulator with
+//   pre  : -D per (row, head), zeroing of the fp32 dQ accumulator, and the
+//          main kernel's schedule (key tiles ranked by their work);
+//   main : one workgroup of 8 waves per (sequence, 256-key tile, kv head),
+//          largest first; wave w owns 32 keys and keeps dK^T and dV^T in
+//          registers (K and V sit in LDS) while the workgroup walks the
+//          32-row query tiles (from the diagonal when causal) of every query
+//          head of its GQA group.  dQ of a query tile is computed by the
+//          whole workgroup from dS staged in LDS (wave w takes d columns
+//          16w..16w+15 over all 256 keys) and added to the accumulator with
 //          fp32 atomics;
 //   post : dQ accumulator -> storage dtype, zeros on pad rows of dK and dV.
 #include <type_traits>
@@ -28,7 +30,7 @@ namespace thd {
 
 namespace {
 
-constexpr int kBwdBK = 128;  // keys per workgroup
+constexpr int kBwdBK = 256;  // keys per workgroup
 constexpr int kBwdBQ = 32;   // query rows per step
 constexpr int kZeroRowsB = 64;
 
@@ -43,7 +45,8 @@ struct BwdParams {
   uint16_t* dk;
   uint16_t* dv;
   float* dq_acc;  // [T_q, h_q, d]
-  float* dsum;    // [h_q, T_q]
+  float* dsum;    // [h_q, T_q], holds -D
+  int32_t* sched; // [2 + 2 * n_kv_tiles]: item count, then (sequence, key tile) by rank
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const int32_t* pad_q;
@@ -54,14 +57,101 @@ struct BwdParams {
   float scale, c2;
   int n_kv_tiles;  // key tiles per kv head (upper bound)
   int n_main;      // n_kv_tiles * h_kv
+  int n_sched;     // leading workgroups of the pre pass that build the schedule
 };
 
 // ---------------------------------------------------------------------------
-// pre: D = rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
+// pre: -D = -rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
 // ---------------------------------------------------------------------------
+// Schedule of the main kernel.  Item (b, kt) -- key tile kt of sequence b --
+// walks W = ceil(lq_b / BQ) query tiles, or max(W - kt * BK / BQ, 0) when b
+// is causal (its first query tile is the diagonal one).  Items are ranked by
+// W, largest first, ties in (b, kt) order, so the longest workgroups start
+// first and the short ones fill in behind them.  A rank is a count:
+//   rank = #{items with larger W} + #{equal W, earlier (b, kt)},
+// and each sequence's share of both counts has a closed form, so no sort is
+// needed.  One wave per sequence b; its lanes take kt = lane, lane + 64, ...
+// sched[0] = number of items kept (at most n_kv_tiles), sched[2 + 2r] and
+// sched[3 + 2r] = (b, kt) of rank r.
+constexpr int kStepQ = kBwdBK / kBwdBQ;  // query tiles per key tile
+
+__device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + b - 1) / b : 0; }
+
+// query tiles ceil(lq / BQ) and key tiles ceil(lk / BK) of sequence b, with
+// the same clamping of lengths as the main kernel
+__device__ __forceinline__ void item_counts(const BwdParams& p, int b, int* nq, int* ntk) {
+  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
+  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+  const int lq = clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 4);
+  const int lk = clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
+  *nq = ceil_div_pos(lq, kBwdBQ);
+  *ntk = ceil_div_pos(lk, kBwdBK);
+}
+
+__device__ void bwd_schedule(const BwdParams& p, int wg) {
+  const int lane = threadIdx.x & 63;
+  const int b = uniform(wg * 4 + (int)(threadIdx.x >> 6));
+  if (b >= p.batch) return;
+  int nq_b, ntk_b;
+  item_counts(p, b, &nq_b, &ntk_b);
+  const bool causal_b = p.causal ? (p.causal[b] != 0) : false;
+  const bool counter = b == 0;  // this wave also writes the item count
+  int rounds = (ntk_b + 63) / 64;
+  if (counter && rounds == 0) rounds = 1;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int kt = 64 * rd + lane;
+    const bool has = kt < ntk_b;
+    const int w = causal_b ? (nq_b - kStepQ * kt > 0 ? nq_b - kStepQ * kt : 0) : nq_b;
+    int64_t rank = causal_b ? (w > 0 ? 0 : kt - min(kt, ceil_div_pos(nq_b, kStepQ))) : kt;
+    int64_t total = 0;
+    for (int c0 = 0; c0 < p.batch; c0 += 64) {
+      // lane j holds sequence c0 + j; every lane then visits all of them
+      int nq_j = 0, ntk_j = 0, cz_j = 0;
+      if (c0 + lane < p.batch) {
+        item_counts(p, c0 + lane, &nq_j, &ntk_j);
+        cz_j = p.causal ? (p.causal[c0 + lane] != 0) : 0;
+      }
+      const int packed = (ntk_j << 1) | cz_j;
+      const int n = min(64, p.batch - c0);
+      for (int j = 0; j < n; ++j) {
+        const int nq = __builtin_amdgcn_readlane(nq_j, j);
+        const int pk = __builtin_amdgcn_readlane(packed, j);
+        const int ntk = pk >> 1;
+        const bool cz = pk & 1;
+        int gt, eq;
+        if (cz) {
+          gt = min(ceil_div_pos(nq - w, kStepQ), ntk);
+          if (w > 0) {
+            const int x = nq - w;
+            eq = (x >= 0 && x % kStepQ == 0 && x / kStepQ < ntk) ? 1 : 0;
+          } else {
+            eq = ntk - min(ntk, ceil_div_pos(nq, kStepQ));
+          }
+        } else {
+          gt = nq > w ? ntk : 0;
+          eq = nq == w ? ntk : 0;
+        }
+        rank += gt + (c0 + j < b ? eq : 0);
+        total += ntk;
+      }
+    }
+    if (has && rank < p.n_kv_tiles) {  // ranks are a permutation of [0, total)
+      int2 e;
+      e.x = b;
+      e.y = kt;
+      *(int2*)(p.sched + 2 + 2 * rank) = e;
+    }
+    if (counter && rd == 0 && lane == 0) p.sched[0] = (int)min(total, (int64_t)p.n_kv_tiles);
+  }
+}
+
 template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
-  const int64_t pair = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  if ((int)blockIdx.x < p.n_sched) {
+    bwd_schedule(p, blockIdx.x);
+    return;
+  }
+  const int64_t pair = (int64_t)(blockIdx.x - p.n_sched) * 16 + (threadIdx.x >> 4);
   const int c = threadIdx.x & 15;
   if (pair >= p.T_q * p.h_q) return;  // whole 16-lane groups leave together
   const int64_t row = pair / p.h_q;
@@ -91,69 +181,68 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (c == 0) p.dsum[(int64_t)hh * p.T_q + row] = valid ? acc : 0.f;
+  if (c == 0) p.dsum[(int64_t)hh * p.T_q + row] = valid ? -acc : 0.f;  // -D
 }
 
 // ---------------------------------------------------------------------------
 // main
 // ---------------------------------------------------------------------------
-// One workgroup of 8 waves per (sequence, 128-key tile, kv head).  The waves
-// form two halves of 4; wave w of a half owns keys 32w .. 32w+31 and keeps
-// dK^T / dV^T for them in registers.  The halves share the K and V tiles in
-// LDS and take alternate query tiles (items 2j + half of the list
-// "every query head of the GQA group x every 32-row query tile from the
-// diagonal"), each with its own double-buffered Q / dO / LSE / D tiles and dS
-// tile, so two waves share each SIMD.  At the end the halves' dK and dV are
-// summed through LDS.
+// One workgroup of 8 waves per (sequence, 256-key tile, kv head); wave w owns
+// keys 32w .. 32w+31 and keeps dK^T / dV^T for them in registers.  All waves
+// walk the same 32-row query tiles (every query head of the GQA group, from
+// the diagonal when causal).  dQ of a query tile is formed by the whole
+// workgroup from dS staged in LDS -- wave w takes d columns 16w .. 16w+15 over
+// all 256 keys with 16x16x32 products -- and added to the fp32 accumulator:
+// one atomic add per (query row, d column) per 256 keys.
 //
-// LDS (bytes, DP = 128): K 32K, V 32K, per half 2 x (Q 8K + dO 8K) + LSE/D
-// 512 + dS 8.5K.  Q, dO, K and V are row-major with swizzled 16-byte chunks;
-// Q^T, dO^T and K^T operands come from transpose reads.
+// LDS (bytes, DP = 128): K 64K and V 64K (resident), Q 8K, dO 8K, dS 16K =
+// 160K.  Q, dO, K and V are row-major with swizzled 16-byte chunks; Q^T, dO^T
+// and K^T operands come from transpose reads.  LSE and D of the lane's 16
+// query rows are read straight into registers.
+template <int DP>
+__device__ __forceinline__ uint32_t swz_ds(int row, int kv) {
+  // dS tile [32][256]: chunk index XOR row%16 keeps 16 rows read at one
+  // logical chunk in 16 distinct bank groups
+  return (uint32_t)row * 512u + ((uint32_t)((kv >> 3) ^ (row & 15)) << 4) + (uint32_t)(kv & 7) * 2;
+}
+
 template <class DT, int DP>
 __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int BK = kBwdBK, BQ = kBwdBQ;
   constexpr int NC = DP / 16;
   constexpr int ND = DP / 32;
   constexpr int KCH = DP / 8;
-  constexpr int SST = BK + 8;   // dS row stride (elements)
   constexpr int TILE = BQ * DP * 2;
   constexpr int OFF_K = 0;
   constexpr int OFF_V = OFF_K + BK * DP * 2;
-  constexpr int OFF_HALF = OFF_V + BK * DP * 2;
-  // half-local layout
-  constexpr int H_Q = 0;
-  constexpr int H_DO = H_Q + 2 * TILE;
-  constexpr int H_LSE = H_DO + 2 * TILE;
-  constexpr int H_D = H_LSE + 2 * BQ * 4;
-  constexpr int H_DS = H_D + 2 * BQ * 4;
-  constexpr int HALF_BYTES = H_DS + BQ * SST * 2;
-  constexpr int SMEM = OFF_HALF + 2 * HALF_BYTES;
-  static_assert(2 * 4 * 64 * ND * 16 * 4 <= SMEM, "dK/dV reduction must fit the LDS");
+  constexpr int OFF_Q = OFF_V + BK * DP * 2;
+  constexpr int OFF_DO = OFF_Q + TILE;
+  constexpr int OFF_DS = OFF_DO + TILE;
+  constexpr int SMEM = OFF_DS + BQ * BK * 2;
+  static_assert(SMEM <= 163840, "LDS budget of one workgroup");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   unsigned char* Kt = smem + OFF_K;
   unsigned char* Vt = smem + OFF_V;
+  unsigned char* Qb = smem + OFF_Q;
+  unsigned char* Ob = smem + OFF_DO;
+  unsigned char* dSs = smem + OFF_DS;
 
+  // Workgroups in schedule order (largest items first), kv heads minor.
   const int bid = blockIdx.x;
-  const int logical = xcd_remap(bid, p.n_main);
-  const int hk = logical / p.n_kv_tiles;
-  const int t = logical - hk * p.n_kv_tiles;
-  int tile_in_seq = 0;
-  const int b = uniform(find_tile(p.cu_kv, p.batch, p.T_kv, BK, t, p.n_kv_tiles, &tile_in_seq));
-  if (b < 0) return;
-  tile_in_seq = uniform(tile_in_seq);
+  const int rk = bid / p.h_kv;
+  const int hk = bid - rk * p.h_kv;
+  if (rk >= p.sched[0]) return;
+  const int b = uniform(p.sched[2 + 2 * rk]);
+  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
+  if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
-  const int wg = uniform(tid >> 6);  // wave in the workgroup, 0..7
-  const int half = wg >> 2;
-  const int w = wg & 3;              // wave in its half: keys 32w .. 32w+31
-  const int ltid = tid & 255;        // thread in its half
+  const int w = uniform(tid >> 6);  // keys 32w .. 32w+31; dQ columns 16w .. 16w+15
   const int l = tid & 63;
   const int r = l & 31;
   const int h = l >> 5;
-  const int g16 = l & 15;            // lane inside its 16-lane group
-  const int grp = l >> 4;            // 16-lane group of the wave
-  unsigned char* hbase = smem + OFF_HALF + half * HALF_BYTES;
-  uint16_t* dSs = (uint16_t*)(hbase + H_DS);
+  const int g16 = l & 15;           // lane inside its 16-lane group
+  const int grp = l >> 4;           // 16-lane group of the wave
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
@@ -168,7 +257,7 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const int kw0 = k0 + 32 * w;
   const int my_k = kw0 + r;
 
-  // Keys [k0, lk) of kv head hk; rows past lk read as zeros.
+  // Keys [k0, lk) of kv head hk -> LDS; rows past lk read as zeros.
   const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
@@ -190,66 +279,28 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const int q_start = causal ? (k0 / BQ) * BQ : 0;
   const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
   const int n_iter = p.group * n_qt;
-  const int n_rounds = (n_iter + 1) / 2;
 
-  // Staging of one query tile by the 256 threads of a half: BQ*KCH chunks of
-  // Q and of dO; threads 256-BQ .. 255 of the half also fetch LSE and D.
-  constexpr int QLOADS = (BQ * KCH + 255) / 256;
-  const int st_lane = ltid - (256 - BQ);
-  u32x4 qreg[QLOADS], oreg[QLOADS];
-  float lse_r = 0.f, d_r = 0.f;
-
+  // Staging of the next query tile: BQ*KCH chunks each of Q and dO.
+  const bool s_loader = tid < BQ * KCH;
+  const int s_row = tid / KCH;
+  const int s_x = tid - s_row * KCH;
+  const uint32_t s_off = (s_loader && 8 * s_x < p.d) ? (uint32_t)s_row * qrow_bytes + 16u * s_x
+                                                      : kOobOffset;
+  u32x4 qreg = {0u, 0u, 0u, 0u}, oreg = {0u, 0u, 0u, 0u};
   auto load_q = [&](int hq, int q0) {
     const int64_t hoff = sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
     const rsrc_t q_rs = make_rsrc(p.q + hoff, (uint32_t)lq * qrow_bytes);
     const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) {
-      const int cid = ltid + 256 * i;
-      const int row = cid / KCH;
-      const int x = cid - row * KCH;
-      const uint32_t off = (cid < BQ * KCH && 8 * x < p.d)
-                               ? (uint32_t)(q0 + row) * qrow_bytes + 16u * x
-                               : kOobOffset;
-      qreg[i] = buf_load16(q_rs, off, 0);
-      oreg[i] = buf_load16(o_rs, off, 0);
-    }
-    if (st_lane >= 0) {
-      const int qi = q0 + st_lane;
-      if (qi < lq) {
-        const int64_t idx = (int64_t)hq * p.T_q + sq + qi;
-        lse_r = p.lse[idx] * kLog2e;
-        d_r = p.dsum[idx];
-      } else {
-        lse_r = __builtin_inff();  // rows past the sequence get P = 0
-        d_r = 0.f;
-      }
+    const uint32_t off = s_off == kOobOffset ? kOobOffset : s_off + (uint32_t)q0 * qrow_bytes;
+    qreg = buf_load16(q_rs, off, 0);
+    oreg = buf_load16(o_rs, off, 0);
+  };
+  auto store_q = [&]() {
+    if (s_loader) {
+      *(u32x4*)(Qb + swz<DP>(s_row, 8 * s_x)) = qreg;
+      *(u32x4*)(Ob + swz<DP>(s_row, 8 * s_x)) = oreg;
     }
   };
-
-  auto store_q = [&](int buf) {
-    unsigned char* Qb = hbase + H_Q + buf * TILE;
-    unsigned char* Ob = hbase + H_DO + buf * TILE;
-#pragma unroll
-    for (int i = 0; i < QLOADS; ++i) {
-      const int cid = ltid + 256 * i;
-      const int row = cid / KCH;
-      const int x = cid - row * KCH;
-      if (cid < BQ * KCH) {
-        *(u32x4*)(Qb + swz<DP>(row, 8 * x)) = qreg[i];
-        *(u32x4*)(Ob + swz<DP>(row, 8 * x)) = oreg[i];
-      }
-    }
-    if (st_lane >= 0) {
-      ((float*)(hbase + H_LSE))[buf * BQ + st_lane] = lse_r;
-      ((float*)(hbase + H_D))[buf * BQ + st_lane] = d_r;
-    }
-  };
-
-  // A half without an item (last round, odd count) still runs the products
-  // on its buffers with everything masked: start them as finite zeros.
-  for (int i = ltid; i < (2 * TILE * 2 + 4 * BQ * 4) / 16; i += 256)
-    ((u32x4*)hbase)[i] = u32x4{0u, 0u, 0u, 0u};
 
   f32x16 dk_acc[ND], dv_acc[ND];
 #pragma unroll
@@ -263,44 +314,53 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const int tr_row = g16 >> 2;
   const int tr_col = 4 * (g16 & 3);
   const float c2 = p.c2;
-  const int dcol = 32 * w + r;  // d column of this lane in the dQ product
 
-  // Item it -> (query head, first query row); a half walks it = half, +2, ...
-  auto item = [&](int it, int& hq_, int& q0_) {
-    const int hi = it / n_qt;
-    hq_ = hk * p.group + hi;
-    q0_ = q_start + (it - hi * n_qt) * BQ;
+  int hq = hk * p.group, q0 = q_start;
+  auto advance = [&](int& hq_, int& q0_) {
+    q0_ += BQ;
+    if (q0_ >= lq) {
+      q0_ = q_start;
+      ++hq_;
+    }
   };
-  int it = half;
-  int hq = 0, q0 = 0;
-  if (it < n_iter) item(it, hq, q0);
-  __syncthreads();  // K / V tiles and zeroed buffers visible
-  if (it < n_iter) {
+  if (n_iter > 0) {
     load_q(hq, q0);
-    store_q(0);
+    store_q();
   }
-  __syncthreads();
-  for (int round = 0; round < n_rounds; ++round, it += 2) {
-    const int buf = round & 1;
-    const bool live = it < n_iter;
-    const bool more = it + 2 < n_iter;
-    int hq_n = 0, q0_n = 0;
-    if (more) {
-      item(it + 2, hq_n, q0_n);
-      load_q(hq_n, q0_n);
+  __syncthreads();  // K, V and the first query tile visible
+  for (int iter = 0; iter < n_iter; ++iter) {
+    const bool more = iter + 1 < n_iter;
+    int hq_n = hq, q0_n = q0;
+    advance(hq_n, q0_n);
+    if (more) load_q(hq_n, q0_n);
+
+    // The products start from the row statistics of this lane's query rows
+    // q0 + 8m + 4h + e (register 4m + e of the C layout): S from -LSE/scale,
+    // so that P = exp2(S * scale * log2 e), and dP from -D (stored negated),
+    // so that dS = P * dP.
+    f32x16 s, dp;
+    {
+      const int64_t roff = (int64_t)hq * p.T_q + sq;
+      const rsrc_t l_rs = make_rsrc(p.lse + roff, (uint32_t)lq * 4u);
+      const rsrc_t d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
+      const float nis = -1.0f / p.scale;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t off = (uint32_t)(q0 + 8 * m + 4 * h) * 4u;
+        const f32x4 lv = __builtin_bit_cast(f32x4, buf_load16(l_rs, off, 0));
+        const f32x4 dv = __builtin_bit_cast(f32x4, buf_load16(d_rs, off, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          s[4 * m + e] = lv[e] * nis;
+          dp[4 * m + e] = dv[e];
+        }
+      }
     }
 
-    const unsigned char* Qb = hbase + H_Q + buf * TILE;
-    const unsigned char* Ob = hbase + H_DO + buf * TILE;
-    const float* lse2s = (const float*)(hbase + H_LSE) + buf * BQ;
-    const float* dds = (const float*)(hbase + H_D) + buf * BQ;
-
     // Every wave runs the products, also when none of its keys is visible to
-    // this query tile or its half has no item (then the mask zeroes P and
-    // dS): the accumulators are updated unconditionally and stay in the MFMA
-    // registers across iterations.
+    // this query tile (then the mask zeroes P and dS): the accumulators are
+    // updated unconditionally and stay in registers across iterations.
     {
-      f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         const u32x4 qa = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
@@ -310,16 +370,18 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         s = DT::mfma(as_vec8<DT>(qa), as_vec8<DT>(ka), s);
         dp = DT::mfma(as_vec8<DT>(oa), as_vec8<DT>(va), dp);
       }
-      const bool need_mask = !live || (kw0 + 32 > lk) || (causal && kw0 + 31 > q0);
+      // mask: key past lk, query row past lq, or (causal) key after the row
+      const bool need_mask = (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0);
       const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
-      const bool key_ok = live && my_k < lk;
+      const int row_hi = lq - q0;                  // visible iff qi < lq - q0
+      const bool key_ok = my_k < lk;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-        float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[i], c2, -lse2s[qi]));
-        if (need_mask) pv = (key_ok && qi >= lim_lo) ? pv : 0.f;
+        float pv = __builtin_amdgcn_exp2f(s[i] * c2);
+        if (need_mask) pv = (key_ok && qi >= lim_lo && qi < row_hi) ? pv : 0.f;
         s[i] = pv;
-        dp[i] = pv * (dp[i] - dds[qi]);
+        dp[i] = pv * dp[i];
       }
       typename DT::vec8 pb[2], db[2];
 #pragma unroll
@@ -350,8 +412,8 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
           dk_acc[dt] = DT::mfma(as_vec8<DT>(tq), db[kb], dk_acc[dt]);
         }
       }
-      // dS (query-major) for the dQ product of this half; elements are taken
-      // from the packed 32-bit words (element j sits in word j/2, half j&1).
+      // dS (query-major) for the dQ product; elements are taken from the
+      // packed 32-bit words (element j sits in word j/2, half j&1).
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 words = __builtin_bit_cast(u32x4, db[kb]);
@@ -359,76 +421,59 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * kb + j;
           const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-          dSs[qi * SST + 32 * w + r] = (uint16_t)(words[j >> 1] >> (16 * (j & 1)));
+          *(uint16_t*)(dSs + swz_ds<DP>(qi, 32 * w + r)) =
+              (uint16_t)(words[j >> 1] >> (16 * (j & 1)));
         }
       }
     }
-    __syncthreads();  // dS complete; every wave is done with this query buffer
-    if (more) store_q(buf ^ 1);
+    __syncthreads();  // dS complete; every wave is done with this query tile
+    if (more) store_q();
 
-    if (live && w < ND) {
-      // dQ[q][32w + r] = sum_kv dS[q][kv] K[kv][32w + r]; B operand lane
-      // (r, h) needs K rows 16kb + 8h + 0..7 at column 32w + r.
+    if (16 * w < DP) {
+      // dQ[q][16w + n] = sum_kv dS[q][kv] K[kv][16w + n] over the workgroup's
+      // keys.  16x16x32 products: A lane l = dS[qh*16 + l%16][32s + 8(l/16) ..],
+      // B lane l = K[32s + 8(l/16) + j][16w + l%16] (two transpose reads).
       int kv_act = lk - k0;
       if (kv_act > BK) kv_act = BK;
       if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
-      const int nkb = (kv_act + 15) / 16;
-      const int c0 = 32 * w + 16 * (grp & 1) + tr_col;
-      f32x16 dq = f32x16{};
+      const int nst = (kv_act + 31) / 32;
+      const int c0 = 16 * w + tr_col;
+      f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
+#pragma unroll 2
+      for (int st = 0; st < nst; ++st) {
+        const int r0 = 32 * st + 8 * grp + tr_row;
+        const u32x4 kt =
+            cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
 #pragma unroll
-      for (int kb = 0; kb < BK / 16; ++kb) {
-        if (kb < nkb) {
-          const u32x4 da = *(const u32x4*)(&dSs[r * SST + 16 * kb + 8 * h]);
-          const int r0 = 16 * kb + 8 * h + tr_row;
-          const u32x4 kt =
-              cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
-          dq = DT::mfma(as_vec8<DT>(da), as_vec8<DT>(kt), dq);
+        for (int qh = 0; qh < 2; ++qh) {
+          const u32x4 da = *(const u32x4*)(dSs + swz_ds<DP>(16 * qh + g16, 32 * st + 8 * grp));
+          dq[qh] = DT::mfma16(as_vec8<DT>(da), as_vec8<DT>(kt), dq[qh]);
         }
       }
       // rows past lq fall outside the resource and are dropped; accumulator
-      // layout [h_q][T_q][DP], so the 4 rows of a group are immediate offsets
+      // layout [h_q][T_q][DP]: the 4 rows of a lane are immediate offsets
+      const int dcol = 16 * w + g16;
       const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq * p.T_q + sq) * DP,
                                       (uint32_t)lq * (DP * 4));
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
+      for (int qh = 0; qh < 2; ++qh) {
         const uint32_t base =
-            dcol < p.d ? (uint32_t)((q0 + 8 * g + 4 * h) * DP + dcol) * 4u : kOobOffset;
+            dcol < p.d ? (uint32_t)((q0 + 16 * qh + 4 * grp) * DP + dcol) * 4u : kOobOffset;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          buf_atomic_add(dq[4 * g + e], acc_rs,
-                         base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
+          buf_atomic_add(dq[qh][e], acc_rs, base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
       }
     }
-    __syncthreads();  // next query buffers visible; dS reads done
+    __syncthreads();  // next query tile visible; dS reads done
     hq = hq_n;
     q0 = q0_n;
   }
 
-  // Sum the halves: half 1 parks its dK, half 0 its dV in LDS (element-major,
-  // lane-contiguous), then half 0 writes dK and half 1 writes dV.
-  float* red = (float*)smem;
-  constexpr int PER = 4 * 64;  // lanes of one half
-  const int slot = w * 64 + l;
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float x = half ? dk_acc[dt][i] : dv_acc[dt][i];
-      red[(half * ND * 16 + dt * 16 + i) * PER + slot] = x;
-    }
-  __syncthreads();
-  f32x16 out[ND];
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float other = red[((1 - half) * ND * 16 + dt * 16 + i) * PER + slot];
-      out[dt][i] = (half ? dv_acc[dt][i] : dk_acc[dt][i]) + other;
-    }
-  const float mul = half ? 1.f : p.scale;  // dK carries the softmax scale
-  uint16_t* dst = half ? p.dv : p.dk;
-  const rsrc_t o_rs = make_rsrc(dst + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                kv_bytes);
+  // Epilogue: this lane's key row of dK (scaled) and dV; rows past lk dropped.
+  const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
+                                 kv_bytes);
+  const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
+                                 kv_bytes);
   const uint32_t krow = (uint32_t)(32 * w + r) * kvrow_bytes;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
@@ -436,12 +481,17 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     for (int gq = 0; gq < 4; ++gq) {
       const int dd = 32 * dt + 8 * gq + 4 * h;
       if (dd < p.d) {
-        u32x2 ov;
-        ov[0] = (uint32_t)DT::bits(out[dt][4 * gq + 0] * mul) |
-                ((uint32_t)DT::bits(out[dt][4 * gq + 1] * mul) << 16);
-        ov[1] = (uint32_t)DT::bits(out[dt][4 * gq + 2] * mul) |
-                ((uint32_t)DT::bits(out[dt][4 * gq + 3] * mul) << 16);
-        buf_store8(ov, o_rs, krow + 2u * dd, 0);
+        u32x2 ok, ov;
+        ok[0] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 0] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 1] * p.scale) << 16);
+        ok[1] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 2] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 3] * p.scale) << 16);
+        ov[0] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 0]) |
+                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 1]) << 16);
+        ov[1] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 2]) |
+                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 3]) << 16);
+        buf_store8(ok, dk_rs, krow + 2u * dd, 0);
+        buf_store8(ov, dv_rs, krow + 2u * dd, 0);
       }
     }
 }
@@ -505,9 +555,9 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   hipError_t em = mark(0);
   if (em != hipSuccess) return em;
   const int64_t pairs = bp.T_q * bp.h_q;
-  if (pairs > 0) {
-    hipLaunchKernelGGL((thd_bwd_pre_kernel<DT, DP>), dim3((unsigned)((pairs + 15) / 16)), dim3(256),
-                       0, s, bp);
+  const int64_t n_pre = bp.n_sched + (pairs + 15) / 16;
+  if (n_pre > 0) {
+    hipLaunchKernelGGL((thd_bwd_pre_kernel<DT, DP>), dim3((unsigned)n_pre), dim3(256), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -536,12 +586,16 @@ int padded_dim(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : 128; }
 
 }  // namespace
 
+static int64_t kv_tile_bound(const Problem& p) { return (p.T_kv + kBwdBK - 1) / kBwdBK + p.batch; }
+
 // fp32 dq accumulator [h_q][T_q][DP] (DP = head_dim rounded up to 32, 64 or
-// 128) followed by D = rowsum(dO * O) [h_q][T_q].
+// 128), then -D = -rowsum(dO * O) [h_q][T_q], then the main kernel's schedule
+// (2 + 2 * key-tile bound int32).
 size_t bwd_workspace_bytes(const Problem& p) {
   const size_t acc = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
   const size_t dsum = align256((size_t)p.T_q * p.h_q * sizeof(float));
-  return acc + dsum;
+  const size_t sched = align256((size_t)(2 + 2 * kv_tile_bound(p)) * sizeof(int32_t));
+  return acc + dsum + sched;
 }
 
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
@@ -558,8 +612,10 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   bp.dk = (uint16_t*)dk;
   bp.dv = (uint16_t*)dv;
   bp.dq_acc = (float*)workspace;
-  bp.dsum = (float*)((char*)workspace +
-                     align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float)));
+  const size_t acc_bytes = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
+  bp.dsum = (float*)((char*)workspace + acc_bytes);
+  bp.sched = (int32_t*)((char*)workspace + acc_bytes +
+                        align256((size_t)p.T_q * p.h_q * sizeof(float)));
   bp.cu_q = p.cu_q;
   bp.cu_kv = p.cu_kv;
   bp.pad_q = p.pad_q;
@@ -574,9 +630,10 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   bp.d = p.d;
   bp.scale = p.scale;
   bp.c2 = p.scale * kLog2e;
-  const int64_t n_kv_tiles = (p.T_kv + kBwdBK - 1) / kBwdBK + p.batch;
+  const int64_t n_kv_tiles = kv_tile_bound(p);
   bp.n_kv_tiles = (int)n_kv_tiles;
   bp.n_main = (p.batch > 0) ? (int)(n_kv_tiles * p.h_kv) : 0;
+  bp.n_sched = (p.batch > 0) ? (p.batch + 3) / 4 : 0;
   if (p.d <= 32) return p.bf16 ? launch_bwd_t<Bf16, 32>(bp, s, ev) : launch_bwd_t<Fp16, 32>(bp, s, ev);
   if (p.d <= 64) return p.bf16 ? launch_bwd_t<Bf16, 64>(bp, s, ev) : launch_bwd_t<Fp16, 64>(bp, s, ev);
   return p.bf16 ? launch_bwd_t<Bf16, 128>(bp, s, ev) : launch_bwd_t<Fp16, 128>(bp, s, ev);

@@ -17,6 +17,7 @@ namespace thd {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -31,6 +32,11 @@ struct Bf16 {
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
   }
+  // 16x16x32: A lane l holds A[l%16][8(l/16) .. +7], B lane l holds
+  // B[8(l/16) .. +7][l%16], C lane l holds C[4(l/16) + i][l%16], i = 0..3.
+  static __device__ __forceinline__ f32x4_t mfma16(vec8 a, vec8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (__bf16)x);
   }
@@ -44,6 +50,9 @@ struct Fp16 {
   typedef f16x8 vec8;
   static __device__ __forceinline__ f32x16 mfma(vec8 a, vec8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4_t mfma16(vec8 a, vec8 b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   static __device__ __forceinline__ uint16_t bits(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
