@@ -46,6 +46,7 @@ struct BwdParams {
   uint16_t* dv;
   float* dq_acc;  // [T_q, h_q, d]
   float* dsum;    // [h_q, T_q], holds -D
+  float* lsum;    // [h_q, T_q], holds -LSE / scale
   int32_t* sched; // [2 + 2 * n_kv_tiles]: item count, then (sequence, key tile) by rank
   const int32_t* cu_q;
   const int32_t* cu_kv;
@@ -182,6 +183,10 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
   if (c == 0) p.dsum[(int64_t)hh * p.T_q + row] = valid ? -acc : 0.f;  // -D
+  if (c == 1) {
+    const int64_t i = (int64_t)hh * p.T_q + row;
+    p.lsum[i] = valid ? p.lse[i] * (-1.0f / p.scale) : 0.f;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -195,15 +200,47 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
 // all 256 keys with 16x16x32 products -- and added to the fp32 accumulator:
 // one atomic add per (query row, d column) per 256 keys.
 //
-// LDS (bytes, DP = 128): K 64K and V 64K (resident), Q 8K, dO 8K, dS 16K =
-// 160K.  Q, dO, K and V are row-major with swizzled 16-byte chunks; Q^T, dO^T
-// and K^T operands come from transpose reads.  LSE and D of the lane's 16
-// query rows are read straight into registers.
+// LDS (bytes, DP = 128): dS 16K, Q 8K, dO 8K, K 64K and V 64K (resident) =
+// 160K, in that order so that every tile but V starts below 64K and can be
+// addressed through the instruction's offset field.  Q, dO, K and V are
+// row-major with swizzled 16-byte chunks; Q^T, dO^T and K^T operands come
+// from transpose reads.
 template <int DP>
 __device__ __forceinline__ uint32_t swz_ds(int row, int kv) {
   // dS tile [32][256]: chunk index XOR row%16 keeps 16 rows read at one
   // logical chunk in 16 distinct bank groups
   return (uint32_t)row * 512u + ((uint32_t)((kv >> 3) ^ (row & 15)) << 4) + (uint32_t)(kv & 7) * 2;
+}
+
+// Swizzled addresses inside the loop.  With the swizzle f(row) an XOR on the
+// chunk index that depends on row bits 0-3 only, each address the loop uses
+// equals a per-lane base XOR a constant: the constant either flips chunk
+// bits or sets row bits that are zero in the base.  The loop therefore keeps
+// a handful of bases live instead of one register per address.
+//   S / dP operands:   swz(r, 16c + 8h)         = swz(r, 8h) ^ (c << 5)
+//                      (same for key row 32w + r, since f(32w + r) = f(r))
+//   dV / dK operands:  swz(R + 16kb + 8j, C + 32dt), R = 4h + tr_row < 8
+//                        = swz(R, C) ^ ((16kb + 8j) * 2DP) ^ ((4dt ^ 8j') << 4)
+//                      with j' = j when DP = 128 (f's bit 3 follows row bit 3)
+//   dS writes:         swz_ds(8m + 4h + e, kv)  = swz_ds(4h, kv) ^ ((8m + e) << 9)
+//                                                 ^ ((8(m & 1) + e) << 4)
+//   dQ, dS reads:      swz_ds(16qh + g, 32st + 8grp) = swz_ds(g, 8grp) ^ (qh << 13)
+//                                                      ^ (st << 6)
+//   dQ, K^T reads:     swz(32st + R' + 4j, C), R' = 8grp + tr_row
+//                        = swz(R', C) ^ ((32st + 4j) * 2DP) ^ (j << 4)
+template <int DP>
+__device__ __forceinline__ uint32_t tr_xor(int dt, int kb, int j) {
+  return (uint32_t)((16 * kb + 8 * j) * DP * 2) ^ ((uint32_t)(4 * dt ^ (DP == 128 ? 8 * j : 0)) << 4);
+}
+__device__ __forceinline__ uint32_t ds_xor(int m, int e) {
+  return ((uint32_t)(8 * m + e) << 9) ^ ((uint32_t)(8 * (m & 1) + e) << 4);
+}
+
+// Makes v opaque to the optimiser: values derived from it are formed where
+// they are used instead of being hoisted out of the loop into registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 template <class DT, int DP>
@@ -213,13 +250,14 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   constexpr int ND = DP / 32;
   constexpr int KCH = DP / 8;
   constexpr int TILE = BQ * DP * 2;
-  constexpr int OFF_K = 0;
-  constexpr int OFF_V = OFF_K + BK * DP * 2;
-  constexpr int OFF_Q = OFF_V + BK * DP * 2;
+  constexpr int OFF_DS = 0;
+  constexpr int OFF_Q = OFF_DS + BQ * BK * 2;
   constexpr int OFF_DO = OFF_Q + TILE;
-  constexpr int OFF_DS = OFF_DO + TILE;
-  constexpr int SMEM = OFF_DS + BQ * BK * 2;
+  constexpr int OFF_K = OFF_DO + TILE;
+  constexpr int OFF_V = OFF_K + BK * DP * 2;
+  constexpr int SMEM = OFF_V + BK * DP * 2;
   static_assert(SMEM <= 163840, "LDS budget of one workgroup");
+  static_assert(OFF_K < 65536, "tiles read through the offset field start below 64K");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   unsigned char* Kt = smem + OFF_K;
   unsigned char* Vt = smem + OFF_V;
@@ -287,11 +325,15 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const uint32_t s_off = (s_loader && 8 * s_x < p.d) ? (uint32_t)s_row * qrow_bytes + 16u * s_x
                                                       : kOobOffset;
   u32x4 qreg = {0u, 0u, 0u, 0u}, oreg = {0u, 0u, 0u, 0u};
-  auto load_q = [&](int hq, int q0) {
+  // Always issued (past the last tile with an out-of-range offset), so that
+  // every path through the loop has the same vector memory operations in
+  // flight and waits can be counted exactly.
+  auto load_q = [&](int hq, int q0, bool real) {
     const int64_t hoff = sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
     const rsrc_t q_rs = make_rsrc(p.q + hoff, (uint32_t)lq * qrow_bytes);
     const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
-    const uint32_t off = s_off == kOobOffset ? kOobOffset : s_off + (uint32_t)q0 * qrow_bytes;
+    const uint32_t off =
+        (s_off == kOobOffset || !real) ? kOobOffset : s_off + (uint32_t)q0 * qrow_bytes;
     qreg = buf_load16(q_rs, off, 0);
     oreg = buf_load16(o_rs, off, 0);
   };
@@ -314,6 +356,13 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const int tr_row = g16 >> 2;
   const int tr_col = 4 * (g16 & 3);
   const float c2 = p.c2;
+  // address bases (relative to their tile)
+  const uint32_t b_q = swz<DP>(r, 8 * h);
+  const uint32_t b_k = swz<DP>(32 * w + r, 8 * h);
+  const uint32_t b_t = swz<DP>(4 * h + tr_row, 16 * (grp & 1) + tr_col);
+  const uint32_t b_s = swz_ds<DP>(4 * h, 32 * w + r);
+  const uint32_t b_d = swz_ds<DP>(g16, 8 * grp);
+  const uint32_t b_kt = swz<DP>(8 * grp + tr_row, 16 * w + tr_col);
 
   int hq = hk * p.group, q0 = q_start;
   auto advance = [&](int& hq_, int& q0_) {
@@ -323,8 +372,32 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       ++hq_;
     }
   };
+  // dQ of a query tile is held in registers until the next iteration has
+  // issued its loads: vector memory operations retire in order, so atomics
+  // issued before those loads would make every wait for them wait for the
+  // atomics as well.  Atomics are always issued; those with nothing to add
+  // (first iteration, d columns past DP) go out of range and are dropped.
+  f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
+  int hq_p = hq, q0_p = q0;  // query tile that dq belongs to
+  const int dcol = 16 * w + g16;
+  auto flush_dq = [&](bool real) {
+    // rows past lq fall outside the resource and are dropped; accumulator
+    // layout [h_q][T_q][DP]: the 4 rows of a lane are immediate offsets
+    const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq_p * p.T_q + sq) * DP,
+                                    (uint32_t)lq * (DP * 4));
+#pragma unroll
+    for (int qh = 0; qh < 2; ++qh) {
+      const uint32_t base = (real && dcol < p.d)
+                                ? (uint32_t)((q0_p + 16 * qh + 4 * grp) * DP + dcol) * 4u
+                                : kOobOffset;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        buf_atomic_add(dq[qh][e], acc_rs, base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
+    }
+  };
+
   if (n_iter > 0) {
-    load_q(hq, q0);
+    load_q(hq, q0, true);
     store_q();
   }
   __syncthreads();  // K, V and the first query tile visible
@@ -332,41 +405,47 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     const bool more = iter + 1 < n_iter;
     int hq_n = hq, q0_n = q0;
     advance(hq_n, q0_n);
-    if (more) load_q(hq_n, q0_n);
+    // A wave none of whose keys is visible to this query tile (past lk, or
+    // all after the tile's last row when causal) skips its products: its dS
+    // columns lie beyond the keys the dQ product reads.
+    const bool active = !(kw0 >= lk || (causal && kw0 > q0 + BQ - 1));
 
     // The products start from the row statistics of this lane's query rows
     // q0 + 8m + 4h + e (register 4m + e of the C layout): S from -LSE/scale,
-    // so that P = exp2(S * scale * log2 e), and dP from -D (stored negated),
-    // so that dS = P * dP.
+    // so that P = exp2(S * scale * log2 e), and dP from -D, so that
+    // dS = P * dP.
     f32x16 s, dp;
     {
       const int64_t roff = (int64_t)hq * p.T_q + sq;
-      const rsrc_t l_rs = make_rsrc(p.lse + roff, (uint32_t)lq * 4u);
+      const rsrc_t l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
       const rsrc_t d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
-      const float nis = -1.0f / p.scale;
+      const uint32_t off = (uint32_t)(q0 + 4 * h) * 4u;
+      f32x4 lv[4], dv[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t off = (uint32_t)(q0 + 8 * m + 4 * h) * 4u;
-        const f32x4 lv = __builtin_bit_cast(f32x4, buf_load16(l_rs, off, 0));
-        const f32x4 dv = __builtin_bit_cast(f32x4, buf_load16(d_rs, off, 0));
+        lv[m] = __builtin_bit_cast(f32x4, buf_load16(l_rs, off + 32u * m, 0));
+        dv[m] = __builtin_bit_cast(f32x4, buf_load16(d_rs, off + 32u * m, 0));
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          s[4 * m + e] = lv[e] * nis;
-          dp[4 * m + e] = dv[e];
+          s[4 * m + e] = lv[m][e];
+          dp[4 * m + e] = dv[m][e];
         }
-      }
     }
+    load_q(hq_n, q0_n, more);
+    flush_dq(iter > 0);
 
-    // Every wave runs the products, also when none of its keys is visible to
-    // this query tile (then the mask zeroes P and dS): the accumulators are
-    // updated unconditionally and stay in registers across iterations.
-    {
+    if (active) {
+      const uint32_t a_q = opaque(b_q), a_k = opaque(b_k);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const u32x4 qa = *(const u32x4*)(Qb + swz<DP>(r, 16 * c + 8 * h));
-        const u32x4 ka = *(const u32x4*)(Kt + swz<DP>(32 * w + r, 16 * c + 8 * h));
-        const u32x4 oa = *(const u32x4*)(Ob + swz<DP>(r, 16 * c + 8 * h));
-        const u32x4 va = *(const u32x4*)(Vt + swz<DP>(32 * w + r, 16 * c + 8 * h));
+        const uint32_t cx = (uint32_t)c << 5;
+        const u32x4 qa = *(const u32x4*)(Qb + (a_q ^ cx));
+        const u32x4 ka = *(const u32x4*)(Kt + (a_k ^ cx));
+        const u32x4 oa = *(const u32x4*)(Ob + (a_q ^ cx));
+        const u32x4 va = *(const u32x4*)(Vt + (a_k ^ cx));
         s = DT::mfma(as_vec8<DT>(qa), as_vec8<DT>(ka), s);
         dp = DT::mfma(as_vec8<DT>(oa), as_vec8<DT>(va), dp);
       }
@@ -398,30 +477,29 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       // dV^T += dO^T P and dK^T += Q^T dS.  A operand lane (r, h) needs
       // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
       // the order in which P / dS hold them: two transpose reads.
+      const uint32_t a_t = opaque(b_t);
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt) {
-        const int c0 = 32 * dt + 16 * (grp & 1) + tr_col;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const int r0 = 16 * kb + 4 * h + tr_row;
-          const u32x4 to =
-              cat2(lds_read_tr(Ob, swz<DP>(r0, c0)), lds_read_tr(Ob, swz<DP>(r0 + 8, c0)));
-          const u32x4 tq =
-              cat2(lds_read_tr(Qb, swz<DP>(r0, c0)), lds_read_tr(Qb, swz<DP>(r0 + 8, c0)));
+          const uint32_t t0 = a_t ^ tr_xor<DP>(dt, kb, 0);
+          const uint32_t t1 = a_t ^ tr_xor<DP>(dt, kb, 1);
+          const u32x4 to = cat2(lds_read_tr(Ob, t0), lds_read_tr(Ob, t1));
+          const u32x4 tq = cat2(lds_read_tr(Qb, t0), lds_read_tr(Qb, t1));
           dv_acc[dt] = DT::mfma(as_vec8<DT>(to), pb[kb], dv_acc[dt]);
           dk_acc[dt] = DT::mfma(as_vec8<DT>(tq), db[kb], dk_acc[dt]);
         }
       }
       // dS (query-major) for the dQ product; elements are taken from the
       // packed 32-bit words (element j sits in word j/2, half j&1).
+      const uint32_t a_s = opaque(b_s);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const u32x4 words = __builtin_bit_cast(u32x4, db[kb]);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int i = 8 * kb + j;
-          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-          *(uint16_t*)(dSs + swz_ds<DP>(qi, 32 * w + r)) =
+          *(uint16_t*)(dSs + (a_s ^ ds_xor(i >> 2, i & 3))) =
               (uint16_t)(words[j >> 1] >> (16 * (j & 1)));
         }
       }
@@ -437,37 +515,29 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       if (kv_act > BK) kv_act = BK;
       if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
       const int nst = (kv_act + 31) / 32;
-      const int c0 = 16 * w + tr_col;
-      f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
+      const uint32_t a_d = opaque(b_d), a_kt = opaque(b_kt);
+      dq[0] = f32x4_t{};
+      dq[1] = f32x4_t{};
 #pragma unroll 2
       for (int st = 0; st < nst; ++st) {
-        const int r0 = 32 * st + 8 * grp + tr_row;
-        const u32x4 kt =
-            cat2(lds_read_tr(Kt, swz<DP>(r0, c0)), lds_read_tr(Kt, swz<DP>(r0 + 4, c0)));
+        const uint32_t k_x = (uint32_t)(32 * st) * (DP * 2);
+        const uint32_t kt0 = a_kt ^ k_x;
+        const uint32_t kt1 = a_kt ^ (k_x ^ ((uint32_t)(4 * DP * 2) | 16u));
+        const u32x4 kt = cat2(lds_read_tr(Kt, kt0), lds_read_tr(Kt, kt1));
 #pragma unroll
         for (int qh = 0; qh < 2; ++qh) {
-          const u32x4 da = *(const u32x4*)(dSs + swz_ds<DP>(16 * qh + g16, 32 * st + 8 * grp));
+          const u32x4 da = *(const u32x4*)(dSs + (a_d ^ (((uint32_t)qh << 13) | ((uint32_t)st << 6))));
           dq[qh] = DT::mfma16(as_vec8<DT>(da), as_vec8<DT>(kt), dq[qh]);
         }
       }
-      // rows past lq fall outside the resource and are dropped; accumulator
-      // layout [h_q][T_q][DP]: the 4 rows of a lane are immediate offsets
-      const int dcol = 16 * w + g16;
-      const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq * p.T_q + sq) * DP,
-                                      (uint32_t)lq * (DP * 4));
-#pragma unroll
-      for (int qh = 0; qh < 2; ++qh) {
-        const uint32_t base =
-            dcol < p.d ? (uint32_t)((q0 + 16 * qh + 4 * grp) * DP + dcol) * 4u : kOobOffset;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          buf_atomic_add(dq[qh][e], acc_rs, base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
-      }
+      hq_p = hq;
+      q0_p = q0;
     }
     __syncthreads();  // next query tile visible; dS reads done
     hq = hq_n;
     q0 = q0_n;
   }
+  if (n_iter > 0) flush_dq(16 * w < DP);
 
   // Epilogue: this lane's key row of dK (scaled) and dV; rows past lk dropped.
   const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
@@ -589,11 +659,11 @@ int padded_dim(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : 128; }
 static int64_t kv_tile_bound(const Problem& p) { return (p.T_kv + kBwdBK - 1) / kBwdBK + p.batch; }
 
 // fp32 dq accumulator [h_q][T_q][DP] (DP = head_dim rounded up to 32, 64 or
-// 128), then -D = -rowsum(dO * O) [h_q][T_q], then the main kernel's schedule
-// (2 + 2 * key-tile bound int32).
+// 128), then -D = -rowsum(dO * O) and -LSE / scale (each [h_q][T_q]), then
+// the main kernel's schedule (2 + 2 * key-tile bound int32).
 size_t bwd_workspace_bytes(const Problem& p) {
   const size_t acc = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
-  const size_t dsum = align256((size_t)p.T_q * p.h_q * sizeof(float));
+  const size_t dsum = align256((size_t)p.T_q * p.h_q * 2 * sizeof(float));
   const size_t sched = align256((size_t)(2 + 2 * kv_tile_bound(p)) * sizeof(int32_t));
   return acc + dsum + sched;
 }
@@ -614,8 +684,9 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   bp.dq_acc = (float*)workspace;
   const size_t acc_bytes = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
   bp.dsum = (float*)((char*)workspace + acc_bytes);
+  bp.lsum = bp.dsum + (size_t)p.T_q * p.h_q;
   bp.sched = (int32_t*)((char*)workspace + acc_bytes +
-                        align256((size_t)p.T_q * p.h_q * sizeof(float)));
+                        align256((size_t)p.T_q * p.h_q * 2 * sizeof(float)));
   bp.cu_q = p.cu_q;
   bp.cu_kv = p.cu_kv;
   bp.pad_q = p.pad_q;
