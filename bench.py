@@ -155,9 +155,11 @@ def main():
                       causal, None, w.batch)
     ws_bytes = int(lib.thd_attn_bwd_workspace_size(args))
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    fws_bytes = int(lib.thd_attn_fwd_workspace_size(args))
+    fws = torch.empty(max(fws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = _stream(dev)
     P = {n: _ptr(t) for n, t in dict(q=q, k=k, v=v, o=o, lse=lse, do=do, dq=dq, dk=dk, dv=dv,
-                                     ws=ws, cu_q=cu_q, cu_kv=cu_kv, mq=mask_q,
+                                     ws=ws, fws=fws, cu_q=cu_q, cu_kv=cu_kv, mq=mask_q,
                                      mkv=mask_kv).items()}
     import ctypes
     n_ev = 6
@@ -178,7 +180,8 @@ def main():
         _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
                    "mask kv")
         evs[0].record(cur)
-        _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], stream), "fwd")
+        _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
+                                    fws_bytes, stream), "fwd")
         evs[1].record(cur)
         _lib.check(lib.thd_attn_bwd_timed(args, P["q"], P["k"], P["v"], P["o"], P["do"],
                                           P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],

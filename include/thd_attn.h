@@ -65,7 +65,7 @@ typedef enum {
   THD_ERR_NULL = -1,        /* a required pointer is NULL                     */
   THD_ERR_SHAPE = -2,       /* a size is negative or inconsistent             */
   THD_ERR_UNSUPPORTED = -3, /* head_dim or dtype outside what is built        */
-  THD_ERR_WORKSPACE = -4,   /* backward workspace missing or too small        */
+  THD_ERR_WORKSPACE = -4,   /* workspace missing, too small or misaligned     */
   THD_ERR_HIP = -5          /* the HIP runtime refused a launch               */
 } thd_status;
 
@@ -102,15 +102,24 @@ typedef struct {
 int thd_padding_mask(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                      uint8_t* mask, void* stream);
 
+/* Bytes of device workspace thd_attn_fwd needs for these arguments (the
+ * order in which its workgroups take the query tiles, a few bytes per tile),
+ * 0 if the arguments are invalid or the batch is empty.  The workspace needs
+ * no initialisation. */
+size_t thd_attn_fwd_workspace_size(const thd_varlen_args* args);
+
 /* Forward [I], [C]: o = softmax(scale * q k^T + mask) v per sequence and head.
  *   o   [total_q, h_q, head_dim]  output, every pad row written as +0;
  *   lse [h_q, total_q] fp32       natural-log log-sum-exp of the scaled
  *                                 scores per query row (-inf on pad rows and
  *                                 rows that see no key); needed by backward.
- * q, k, v are read only at valid rows.  Errors: THD_ERR_NULL, THD_ERR_SHAPE,
- * THD_ERR_UNSUPPORTED, THD_ERR_HIP. */
+ * q, k, v are read only at valid rows.  workspace must be a device buffer of
+ * at least thd_attn_fwd_workspace_size(args) bytes, 256-byte aligned, used by
+ * this call only (it may be NULL when that size is 0).  Errors: THD_ERR_NULL,
+ * THD_ERR_SHAPE, THD_ERR_UNSUPPORTED, THD_ERR_WORKSPACE, THD_ERR_HIP. */
 int thd_attn_fwd(const thd_varlen_args* args, const void* q, const void* k,
-                 const void* v, void* o, float* lse, void* stream);
+                 const void* v, void* o, float* lse, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /* Bytes of device workspace thd_attn_bwd needs for these arguments (an fp32
  * dq accumulator and per-row fp32 statistics), 0 if the arguments are
@@ -123,7 +132,7 @@ size_t thd_attn_bwd_workspace_size(const thd_varlen_args* args);
  * of q, k, v; every pad row is written as +0, key/value gradients of a GQA
  * group are summed over its query heads.  workspace must be a device buffer
  * of at least thd_attn_bwd_workspace_size(args) bytes, 256-byte aligned,
- * used by this call only.  Errors: as thd_attn_fwd plus THD_ERR_WORKSPACE. */
+ * used by this call only.  Errors: as thd_attn_fwd. */
 int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k,
                  const void* v, const void* o, const void* dout, const float* lse,
                  void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,

@@ -20,7 +20,7 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     names = declared_functions()
-    for n in ("thd_attn_fwd", "thd_attn_bwd", "thd_padding_mask",
+    for n in ("thd_attn_fwd", "thd_attn_bwd", "thd_padding_mask", "thd_attn_fwd_workspace_size",
               "thd_attn_bwd_workspace_size", "thd_status_string", "thd_version"):
         assert n in names
     assert set(names) == set(_lib.EXPORTED)
@@ -69,26 +69,42 @@ P = ctypes.c_void_p(0x2000)   # never dereferenced: every call below fails valid
 def test_fwd_rejects_invalid_arguments(kw, status):
     lib = _lib.load()
     a = _args(**kw)
-    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, None) == status
+    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, P, 1 << 30, None) == status
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, 1 << 30, None) == status
 
 
 def test_null_and_misaligned_tensors():
     lib = _lib.load()
     a = _args()
-    assert lib.thd_attn_fwd(ctypes.byref(a), None, P, P, P, P, None) == -1
-    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, None, None) == -1
+    big = 1 << 30
+    assert lib.thd_attn_fwd(ctypes.byref(a), None, P, P, P, P, P, big, None) == -1
+    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, None, P, big, None) == -1
     odd = ctypes.c_void_p(0x2002)
-    assert lib.thd_attn_fwd(ctypes.byref(a), odd, P, P, P, P, None) == -3
-    assert lib.thd_attn_fwd(None, P, P, P, P, P, None) == -1
+    assert lib.thd_attn_fwd(ctypes.byref(a), odd, P, P, P, P, P, big, None) == -3
+    assert lib.thd_attn_fwd(None, P, P, P, P, P, P, big, None) == -1
+
+
+def test_fwd_workspace_size_and_check():
+    lib = _lib.load()
+    a = _args()
+    need = lib.thd_attn_fwd_workspace_size(ctypes.byref(a))
+    # item count and (sequence, tile) pairs for up to T_q/128 + batch query tiles
+    assert need >= (2 + 2 * (1 + 2)) * 4
+    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(batch=-1))) == 0
+    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(batch=0))) == 0
+    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, P, need - 1, None) == -4
+    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, None, need, None) == -4
+    mis = ctypes.c_void_p(0x2010)
+    assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, mis, need, None) == -4
 
 
 def test_workspace_size_and_check():
     lib = _lib.load()
     a = _args()
     need = lib.thd_attn_bwd_workspace_size(ctypes.byref(a))
-    # fp32 dq accumulator [T_q, h_q, d] plus fp32 row statistics [h_q, T_q]
-    assert need >= 16 * 4 * 64 * 4 + 16 * 4 * 4
+    # fp32 dq accumulator [T_q, h_q, d], two fp32 row statistics [h_q, T_q]
+    # and the schedule of the key tiles
+    assert need >= 16 * 4 * 64 * 4 + 2 * 16 * 4 * 4 + (2 + 2 * (1 + 2)) * 4
     assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(batch=-1))) == 0
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, need - 1, None) == -4
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, None, need, None) == -4

@@ -112,12 +112,14 @@ def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
 
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, *,
              cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None, is_causal=None,
-             softmax_scale=None, batch_size=None, out=None, lse=None):
+             softmax_scale=None, batch_size=None, out=None, lse=None, workspace=None):
     """Forward attention; returns (out [T_q,h_q,d], lse [h_q,T_q] fp32).
 
     ``is_causal``: one bool/uint8 per sequence (None = all ``padding``).
     ``softmax_scale``: None = 1/sqrt(head_dim).  ``batch_size``: number of
     sequences when the cu_seqlens buffers are longer than batch + 1.
+    ``workspace``: uint8 device buffer of at least ``fwd_workspace_size``
+    bytes (allocated here when None).
     """
     a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                    cu_seqlens_q_padded, cu_seqlens_kv_padded, is_causal, softmax_scale,
@@ -134,9 +136,19 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, 
     if out.shape != q.shape or lse.shape != (q.shape[1], q.shape[0]):
         raise ValueError("out / lse have the wrong shape")
     lib = _lib.load()
-    st = lib.thd_attn_fwd(a, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _stream(q.device))
+    need = int(lib.thd_attn_fwd_workspace_size(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _require_cuda("workspace", workspace, torch.uint8)
+    st = lib.thd_attn_fwd(a, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
+                          workspace.numel(), _stream(q.device))
     _lib.check(st, "thd_attn_fwd")
     return out, lse
+
+
+def fwd_workspace_size(q, k, cu_seqlens_q, cu_seqlens_kv, batch_size=None):
+    a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, 0, 0, None, None, None, None, batch_size)
+    return int(_lib.load().thd_attn_fwd_workspace_size(a))
 
 
 def bwd_workspace_size(q, k, cu_seqlens_q, cu_seqlens_kv, batch_size=None):

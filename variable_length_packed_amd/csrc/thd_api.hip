@@ -85,8 +85,14 @@ int thd_padding_mask(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqle
   return e == hipSuccess ? THD_OK : THD_ERR_HIP;
 }
 
+size_t thd_attn_fwd_workspace_size(const thd_varlen_args* args) {
+  thd::Problem p;
+  if (to_problem(args, &p) != THD_OK) return 0;
+  return thd::fwd_workspace_bytes(p);
+}
+
 int thd_attn_fwd(const thd_varlen_args* args, const void* q, const void* k, const void* v,
-                 void* o, float* lse, void* stream) {
+                 void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   thd::Problem p;
   int st = to_problem(args, &p);
   if (st != THD_OK) return st;
@@ -95,7 +101,12 @@ int thd_attn_fwd(const thd_varlen_args* args, const void* q, const void* k, cons
       (st = check_tensor(v, Tk)))
     return st;
   if (Tq > 0 && !lse) return THD_ERR_NULL;
-  hipError_t e = thd::launch_fwd(p, q, k, v, o, lse, (hipStream_t)stream);
+  const size_t need = thd::fwd_workspace_bytes(p);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return THD_ERR_WORKSPACE;
+    if (((uintptr_t)workspace & 255u) != 0) return THD_ERR_WORKSPACE;
+  }
+  hipError_t e = thd::launch_fwd(p, q, k, v, o, lse, workspace, (hipStream_t)stream);
   return e == hipSuccess ? THD_OK : THD_ERR_HIP;
 }
 

@@ -64,92 +64,54 @@ struct BwdParams {
 // ---------------------------------------------------------------------------
 // pre: -D = -rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
 // ---------------------------------------------------------------------------
-// Schedule of the main kernel.  Item (b, kt) -- key tile kt of sequence b --
-// walks W = ceil(lq_b / BQ) query tiles, or max(W - kt * BK / BQ, 0) when b
-// is causal (its first query tile is the diagonal one).  Items are ranked by
-// W, largest first, ties in (b, kt) order, so the longest workgroups start
-// first and the short ones fill in behind them.  A rank is a count:
-//   rank = #{items with larger W} + #{equal W, earlier (b, kt)},
-// and each sequence's share of both counts has a closed form, so no sort is
-// needed.  One wave per sequence b; its lanes take kt = lane, lane + 64, ...
-// sched[0] = number of items kept (at most n_kv_tiles), sched[2 + 2r] and
-// sched[3 + 2r] = (b, kt) of rank r.
+// Schedule of the main kernel (largest first, see build_schedule): tile kt
+// of sequence b walks W = ceil(lq / BQ) query tiles, or max(W - kt * BK/BQ, 0)
+// when b is causal (its first query tile is the diagonal one).  Summary:
+// x = ceil(lq / BQ), y = ceil(lk / BK), with the main kernel's clamping.
 constexpr int kStepQ = kBwdBK / kBwdBQ;  // query tiles per key tile
 
-__device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + b - 1) / b : 0; }
-
-// query tiles ceil(lq / BQ) and key tiles ceil(lk / BK) of sequence b, with
-// the same clamping of lengths as the main kernel
-__device__ __forceinline__ void item_counts(const BwdParams& p, int b, int* nq, int* ntk) {
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 4);
-  const int lk = clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
-  *nq = ceil_div_pos(lq, kBwdBQ);
-  *ntk = ceil_div_pos(lk, kBwdBK);
-}
-
-__device__ void bwd_schedule(const BwdParams& p, int wg) {
-  const int lane = threadIdx.x & 63;
-  const int b = uniform(wg * 4 + (int)(threadIdx.x >> 6));
-  if (b >= p.batch) return;
-  int nq_b, ntk_b;
-  item_counts(p, b, &nq_b, &ntk_b);
-  const bool causal_b = p.causal ? (p.causal[b] != 0) : false;
-  const bool counter = b == 0;  // this wave also writes the item count
-  int rounds = (ntk_b + 63) / 64;
-  if (counter && rounds == 0) rounds = 1;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int kt = 64 * rd + lane;
-    const bool has = kt < ntk_b;
-    const int w = causal_b ? (nq_b - kStepQ * kt > 0 ? nq_b - kStepQ * kt : 0) : nq_b;
-    int64_t rank = causal_b ? (w > 0 ? 0 : kt - min(kt, ceil_div_pos(nq_b, kStepQ))) : kt;
-    int64_t total = 0;
-    for (int c0 = 0; c0 < p.batch; c0 += 64) {
-      // lane j holds sequence c0 + j; every lane then visits all of them
-      int nq_j = 0, ntk_j = 0, cz_j = 0;
-      if (c0 + lane < p.batch) {
-        item_counts(p, c0 + lane, &nq_j, &ntk_j);
-        cz_j = p.causal ? (p.causal[c0 + lane] != 0) : 0;
-      }
-      const int packed = (ntk_j << 1) | cz_j;
-      const int n = min(64, p.batch - c0);
-      for (int j = 0; j < n; ++j) {
-        const int nq = __builtin_amdgcn_readlane(nq_j, j);
-        const int pk = __builtin_amdgcn_readlane(packed, j);
-        const int ntk = pk >> 1;
-        const bool cz = pk & 1;
-        int gt, eq;
-        if (cz) {
-          gt = min(ceil_div_pos(nq - w, kStepQ), ntk);
-          if (w > 0) {
-            const int x = nq - w;
-            eq = (x >= 0 && x % kStepQ == 0 && x / kStepQ < ntk) ? 1 : 0;
-          } else {
-            eq = ntk - min(ntk, ceil_div_pos(nq, kStepQ));
-          }
-        } else {
-          gt = nq > w ? ntk : 0;
-          eq = nq == w ? ntk : 0;
-        }
-        rank += gt + (c0 + j < b ? eq : 0);
-        total += ntk;
-      }
-    }
-    if (has && rank < p.n_kv_tiles) {  // ranks are a permutation of [0, total)
-      int2 e;
-      e.x = b;
-      e.y = kt;
-      *(int2*)(p.sched + 2 + 2 * rank) = e;
-    }
-    if (counter && rd == 0 && lane == 0) p.sched[0] = (int)min(total, (int64_t)p.n_kv_tiles);
+struct BwdSchedModel {
+  const BwdParams& p;
+  __device__ SeqSummary seq(int b) const {
+    const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
+    const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+    const int lq =
+        clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 4);
+    const int lk =
+        clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
+    SeqSummary s;
+    s.x = ceil_div_pos(lq, kBwdBQ);
+    s.y = ceil_div_pos(lk, kBwdBK);
+    s.causal = p.causal ? (p.causal[b] != 0) : false;
+    return s;
   }
-}
+  static __device__ int items(const SeqSummary& s) { return s.y; }
+  static __device__ int work(const SeqSummary& s, int t) {
+    return s.causal ? max(s.x - kStepQ * t, 0) : s.x;
+  }
+  static __device__ int gt(const SeqSummary& s, int w) {
+    if (!s.causal) return s.x > w ? s.y : 0;
+    return min(ceil_div_pos(s.x - w, kStepQ), s.y);
+  }
+  static __device__ int eq(const SeqSummary& s, int w) {
+    if (!s.causal) return s.x == w ? s.y : 0;
+    if (w > 0) {
+      const int d = s.x - w;
+      return (d >= 0 && d % kStepQ == 0 && d / kStepQ < s.y) ? 1 : 0;
+    }
+    return s.y - min(s.y, ceil_div_pos(s.x, kStepQ));  // tiles with nothing to walk
+  }
+  static __device__ int before(const SeqSummary& s, int t, int w) {
+    if (!s.causal) return t;
+    return w > 0 ? 0 : t - min(t, ceil_div_pos(s.x, kStepQ));
+  }
+};
 
 template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   if ((int)blockIdx.x < p.n_sched) {
-    bwd_schedule(p, blockIdx.x);
+    build_schedule(BwdSchedModel{p}, p.batch, p.n_kv_tiles, p.sched,
+                   blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
   const int64_t pair = (int64_t)(blockIdx.x - p.n_sched) * 16 + (threadIdx.x >> 4);

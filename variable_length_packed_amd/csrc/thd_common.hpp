@@ -83,16 +83,6 @@ __device__ __forceinline__ float wave_swap_halves(float x) {
   return __shfl_xor(x, 32, 64);
 }
 
-__device__ __forceinline__ int wave_inclusive_scan(int x) {
-  const int l = lane_id();
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    int y = __shfl_up(x, off, 64);
-    if (l >= off) x += y;
-  }
-  return x;
-}
-
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 // ---------------------------------------------------------------------------
@@ -190,35 +180,6 @@ __device__ __forceinline__ int64_t seq_start(const int32_t* cu, const int32_t* c
   return (int64_t)(cu_padded ? cu_padded[b] : cu[b]);
 }
 
-// Map tile index t (over all sequences, in order) to (sequence, tile inside
-// the sequence) for tiles of `rows` query rows.  The whole wave participates
-// and gets the same answer.  Returns -1 when t is past the last tile.
-__device__ __forceinline__ int find_tile(const int32_t* cu, int batch, int64_t cap,
-                                         int rows, int t, int tile_cap, int* tile_in_seq) {
-  const int l = lane_id();
-  int base = 0;
-  for (int b0 = 0; b0 < batch; b0 += 64) {
-    const int b = b0 + l;
-    int n = 0;
-    if (b < batch) {
-      const int len = seq_len_clamped(cu, b, cap);
-      n = (len + rows - 1) / rows;
-      if (n > tile_cap) n = tile_cap;
-    }
-    const int incl = wave_inclusive_scan(n);
-    const int total = __shfl(incl, 63, 64);
-    if (t < base + total) {
-      const uint64_t hit = __ballot(base + incl > t);
-      const int first = __builtin_ctzll(hit);
-      const int excl = __shfl(incl - n, first, 64);
-      *tile_in_seq = t - base - excl;
-      return b0 + first;
-    }
-    base += total;
-  }
-  return -1;
-}
-
 // True when row r lies inside some sequence: the last sequence whose start is
 // <= r (starts non-decreasing) must also cover r.
 __device__ __forceinline__ bool row_is_valid(const int32_t* cu, const int32_t* cu_padded,
@@ -237,13 +198,72 @@ __device__ __forceinline__ bool row_is_valid(const int32_t* cu, const int32_t* c
   return r < seq_start(cu, cu_padded, found) + seq_len_clamped(cu, found, cap);
 }
 
-// XCD-aware remap: hardware hands consecutive workgroup ids to the 8 XCDs in
-// turn; give each XCD a contiguous range of logical ids instead so that work
-// sharing K/V (same sequence and head) shares one L2.
-__device__ __forceinline__ int xcd_remap(int b, int n) {
-  const int full = (n / 8) * 8;
-  if (b >= full) return b;
-  return (b % 8) * (full / 8) + b / 8;
+// ---------------------------------------------------------------------------
+// Largest-first schedules.  The tiles (sequence b, tile t) of a kernel are
+// ranked by their work W, largest first, ties in (b, t) order, and rank r is
+// run by the workgroups r * heads .. r * heads + heads - 1, so the longest
+// workgroups start first and the short ones fill in behind them (greedy list
+// scheduling in decreasing order).  A rank is a count,
+//   rank = #{tiles with larger W} + #{equal W, earlier (b, t)},
+// and a Model gives each sequence's share of both counts in closed form from
+// a summary of the sequence, so no sort is needed:
+//   md.seq(b)          summary {x, y, causal} of sequence b
+//   Model::items(s)    number of tiles of the sequence
+//   Model::work(s, t)  W of tile t
+//   Model::gt(s, w)    #{t : W(t) > w}
+//   Model::eq(s, w)    #{t : W(t) == w}
+//   Model::before(s, t, w)  #{t' < t : W(t') == w}
+// Output: sched[0] = number of tiles kept (at most cap), then (b, t) of rank
+// r at sched[2 + 2r], sched[3 + 2r].  One wave per sequence (wave_id = b);
+// its lanes take t = lane, lane + 64, ...; the wave of sequence 0 also
+// writes sched[0].
+// ---------------------------------------------------------------------------
+struct SeqSummary {
+  int x, y;  // model-defined tile counts, y < 2^30
+  bool causal;
+};
+
+template <class Model>
+__device__ void build_schedule(const Model& md, int batch, int cap, int32_t* sched, int wave_id) {
+  const int lane = lane_id();
+  const int b = uniform(wave_id);
+  if (b >= batch) return;
+  const SeqSummary sb = md.seq(b);
+  const int nb = Model::items(sb);
+  const bool counter = b == 0;
+  int rounds = (nb + 63) / 64;
+  if (counter && rounds == 0) rounds = 1;
+  for (int rd = 0; rd < rounds; ++rd) {
+    const int t = 64 * rd + lane;
+    const int w = Model::work(sb, t);  // unused when t >= nb
+    int64_t rank = Model::before(sb, t, w);
+    int64_t total = 0;
+    for (int c0 = 0; c0 < batch; c0 += 64) {
+      // lane j summarises sequence c0 + j; every lane then visits all of them
+      SeqSummary sj = {0, 0, false};
+      if (c0 + lane < batch) sj = md.seq(c0 + lane);
+      const int px = sj.x, py = (sj.y << 1) | (sj.causal ? 1 : 0);
+      const int n = min(64, batch - c0);
+      for (int j = 0; j < n; ++j) {
+        SeqSummary o;
+        o.x = __builtin_amdgcn_readlane(px, j);
+        const int y = __builtin_amdgcn_readlane(py, j);
+        o.y = y >> 1;
+        o.causal = (y & 1) != 0;
+        rank += Model::gt(o, w) + (c0 + j < b ? Model::eq(o, w) : 0);
+        total += Model::items(o);
+      }
+    }
+    if (t < nb && rank < cap) {  // ranks are a permutation of [0, total)
+      int2 e;
+      e.x = b;
+      e.y = t;
+      *(int2*)(sched + 2 + 2 * rank) = e;
+    }
+    if (counter && rd == 0 && lane == 0) sched[0] = (int)min(total, (int64_t)cap);
+  }
 }
+
+__device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + b - 1) / b : 0; }
 
 }  // namespace thd

@@ -9,13 +9,15 @@
 // tensor is read and the host never synchronises.
 //
 // One workgroup = 4 waves = one (sequence, 128-row query tile, query head)
-// work item, decoded on the device from cu_seqlens_q.  Each wave owns 32
+// work item.  A pre pass ranks the (sequence, query tile) items by the number
+// of key tiles they walk, largest first, and the attention workgroups take
+// them in that order, query heads minor.  Each wave owns 32
 // query rows.  Scores are computed transposed, S^T = K Q^T, so that a lane
 // owns one query row: the row max needs one exchange between wave halves and
 // the probabilities land directly in the B-operand layout of O^T = V^T P^T.
 // K tiles are staged in LDS row-major, V tiles transposed (with the K-slot
-// permutation that matches the accumulator layout of S^T).  Extra workgroups
-// at the end of the grid write zeros to pad rows of O and -inf to their LSE.
+// permutation that matches the accumulator layout of S^T).  The pre pass also
+// writes zeros to pad rows of O and -inf to their LSE.
 #include "thd_common.hpp"
 #include "thd_launch.hpp"
 
@@ -44,6 +46,50 @@ struct FwdParams {
   float scale, c2;  // c2 = scale * log2(e)
   int n_tiles;      // query tiles per head (upper bound over all layouts)
   int n_attn;       // n_tiles * h_q workgroups doing attention
+  int n_sched;      // workgroups of the pre pass building the schedule
+  int32_t* sched;   // [2 + 2 * n_tiles]: item count, then (sequence, tile) by rank
+};
+
+// Schedule of the attention workgroups (largest first, see build_schedule):
+// query tile t of sequence b walks W = ceil(lk / BN) key tiles, or
+// min(W, 2t + 2) when b is causal (keys up to the tile's last row, BM = 2 BN).
+// Summary: x = ceil(lq / BM), y = ceil(lk / BN), with the kernel's clamping.
+static_assert(kFwdBM == 2 * kFwdBN, "work model assumes two key tiles per query tile");
+
+struct FwdSchedModel {
+  const FwdParams& p;
+  __device__ SeqSummary seq(int b) const {
+    const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
+    const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+    const int lq =
+        clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 2);
+    const int lk =
+        clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
+    SeqSummary s;
+    s.x = ceil_div_pos(lq, kFwdBM);
+    s.y = ceil_div_pos(lk, kFwdBN);
+    s.causal = p.causal ? (p.causal[b] != 0) : false;
+    return s;
+  }
+  // first tile of the causal plateau W = y
+  static __device__ int plateau(const SeqSummary& s) { return max((s.y + 1) / 2 - 1, 0); }
+  static __device__ int items(const SeqSummary& s) { return s.x; }
+  static __device__ int work(const SeqSummary& s, int t) {
+    return s.causal ? min(s.y, 2 * t + 2) : s.y;
+  }
+  static __device__ int gt(const SeqSummary& s, int w) {
+    if (s.y <= w) return 0;
+    return s.causal ? max(s.x - w / 2, 0) : s.x;
+  }
+  static __device__ int eq(const SeqSummary& s, int w) {
+    if (!s.causal) return s.y == w ? s.x : 0;
+    if (w < s.y) return (w >= 2 && (w & 1) == 0 && w / 2 - 1 < s.x) ? 1 : 0;
+    return w == s.y ? s.x - min(s.x, plateau(s)) : 0;
+  }
+  static __device__ int before(const SeqSummary& s, int t, int w) {
+    if (!s.causal) return t;
+    return w == s.y ? t - min(t, plateau(s)) : 0;
+  }
 };
 
 // Position of key group g4 (4 keys) inside a 16-key block of the transposed
@@ -82,6 +128,16 @@ __device__ void fwd_zero_pad_rows(const FwdParams& p, int zb) {
   }
 }
 
+// pre: schedule of the attention workgroups, then zeros on pad rows.
+__global__ __launch_bounds__(256) void thd_fwd_pre_kernel(FwdParams p) {
+  if ((int)blockIdx.x < p.n_sched) {
+    build_schedule(FwdSchedModel{p}, p.batch, p.n_tiles, p.sched,
+                   blockIdx.x * 4 + (int)(threadIdx.x >> 6));
+    return;
+  }
+  fwd_zero_pad_rows(p, blockIdx.x - p.n_sched);
+}
+
 // Threshold (log2 units) by which a row maximum must grow before the running
 // maximum is moved and the accumulator rescaled; below it the stale maximum
 // stays, probabilities may reach 2^8, which fp32 sums and 16-bit P hold.
@@ -101,19 +157,16 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
 
+  // Workgroups in schedule order (largest items first), query heads minor:
+  // with h_q a multiple of 8, head hq always lands on XCD hq % 8, whose L2
+  // then holds that head's K and V.
   const int bid = blockIdx.x;
-  if (bid >= p.n_attn) {
-    fwd_zero_pad_rows(p, bid - p.n_attn);
-    return;
-  }
-  // Heaviest work first: within a head, walk query tiles from the last one.
-  const int logical = xcd_remap(bid, p.n_attn);
-  const int hq = logical / p.n_tiles;
-  const int t = p.n_tiles - 1 - (logical - hq * p.n_tiles);
-  int tile_in_seq = 0;
-  const int b = uniform(find_tile(p.cu_q, p.batch, p.T_q, BM, t, p.n_tiles, &tile_in_seq));
-  if (b < 0) return;
-  tile_in_seq = uniform(tile_in_seq);
+  const int rk = bid / p.h_q;
+  const int hq = bid - rk * p.h_q;
+  if (rk >= p.sched[0]) return;
+  const int b = uniform(p.sched[2 + 2 * rk]);
+  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
+  if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -334,15 +387,22 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
 }
 
 template <class DT, int DP>
-hipError_t launch_fwd_t(const FwdParams& fp, int grid, hipStream_t s) {
-  hipLaunchKernelGGL((thd_fwd_kernel<DT, DP>), dim3(grid), dim3(256), 0, s, fp);
+hipError_t launch_fwd_t(const FwdParams& fp, hipStream_t s) {
+  hipLaunchKernelGGL((thd_fwd_kernel<DT, DP>), dim3(fp.n_attn), dim3(256), 0, s, fp);
   return hipGetLastError();
 }
 
+int64_t fwd_tile_bound(const Problem& p) { return (p.T_q + kFwdBM - 1) / kFwdBM + p.batch; }
+
 }  // namespace
 
+// The attention workgroups' schedule: 2 + 2 * query-tile bound int32.
+size_t fwd_workspace_bytes(const Problem& p) {
+  return p.batch > 0 ? (size_t)(2 + 2 * fwd_tile_bound(p)) * sizeof(int32_t) : 0;
+}
+
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
-                      float* lse, hipStream_t s) {
+                      float* lse, void* workspace, hipStream_t s) {
   FwdParams fp;
   fp.q = (const uint16_t*)q;
   fp.k = (const uint16_t*)k;
@@ -363,15 +423,22 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
   fp.d = p.d;
   fp.scale = p.scale;
   fp.c2 = p.scale * kLog2e;
-  const int64_t n_tiles = (p.T_q + kFwdBM - 1) / kFwdBM + p.batch;
+  const int64_t n_tiles = fwd_tile_bound(p);
   fp.n_tiles = (int)n_tiles;
   fp.n_attn = (p.batch > 0) ? (int)(n_tiles * p.h_q) : 0;
+  fp.n_sched = (p.batch > 0) ? (p.batch + 3) / 4 : 0;
+  fp.sched = (int32_t*)workspace;
   const int64_t n_zero = (p.T_q + kZeroRows - 1) / kZeroRows;
-  const int64_t grid = fp.n_attn + n_zero;
-  if (grid == 0) return hipSuccess;
-  if (p.d <= 32) return p.bf16 ? launch_fwd_t<Bf16, 32>(fp, (int)grid, s) : launch_fwd_t<Fp16, 32>(fp, (int)grid, s);
-  if (p.d <= 64) return p.bf16 ? launch_fwd_t<Bf16, 64>(fp, (int)grid, s) : launch_fwd_t<Fp16, 64>(fp, (int)grid, s);
-  return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, (int)grid, s) : launch_fwd_t<Fp16, 128>(fp, (int)grid, s);
+  const int64_t n_pre = fp.n_sched + n_zero;
+  if (n_pre > 0) {
+    hipLaunchKernelGGL(thd_fwd_pre_kernel, dim3((unsigned)n_pre), dim3(256), 0, s, fp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (fp.n_attn == 0) return hipSuccess;
+  if (p.d <= 32) return p.bf16 ? launch_fwd_t<Bf16, 32>(fp, s) : launch_fwd_t<Fp16, 32>(fp, s);
+  if (p.d <= 64) return p.bf16 ? launch_fwd_t<Bf16, 64>(fp, s) : launch_fwd_t<Fp16, 64>(fp, s);
+  return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, s) : launch_fwd_t<Fp16, 128>(fp, s);
 }
 
 }  // namespace thd

@@ -24,8 +24,10 @@ struct Problem {
 hipError_t launch_padding_mask(const int32_t* cu, int batch, int max_seqlen, uint8_t* mask,
                                hipStream_t s);
 
+size_t fwd_workspace_bytes(const Problem& p);
+
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
-                      float* lse, hipStream_t s);
+                      float* lse, void* workspace, hipStream_t s);
 
 size_t bwd_workspace_bytes(const Problem& p);
 
