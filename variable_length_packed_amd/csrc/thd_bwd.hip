@@ -358,7 +358,35 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     }
   };
 
+  // The products start from the row statistics of this lane's query rows
+  // q0 + 8m + 4h + e (register 4m + e of the C layout): S from -LSE/scale,
+  // so that P = exp2(S * scale * log2 e), and dP from -D, so that
+  // dS = P * dP.  They are loaded one query tile ahead, into the S and dP
+  // registers themselves once the previous tile is done with them; the last
+  // load goes out of range.
+  f32x16 s, dp;
+  auto load_stats = [&](int hq_, int q0_, bool real) {
+    const int64_t roff = real ? (int64_t)hq_ * p.T_q + sq : 0;
+    const rsrc_t l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
+    const rsrc_t d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
+    const uint32_t off = real ? (uint32_t)(q0_ + 4 * h) * 4u : kOobOffset;
+    f32x4 lv[4], dv[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      lv[m] = __builtin_bit_cast(f32x4, buf_load16(l_rs, real ? off + 32u * m : kOobOffset, 0));
+      dv[m] = __builtin_bit_cast(f32x4, buf_load16(d_rs, real ? off + 32u * m : kOobOffset, 0));
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        s[4 * m + e] = lv[m][e];
+        dp[4 * m + e] = dv[m][e];
+      }
+  };
+
   if (n_iter > 0) {
+    load_stats(hq, q0, true);
     load_q(hq, q0, true);
     store_q();
   }
@@ -372,30 +400,6 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     // columns lie beyond the keys the dQ product reads.
     const bool active = !(kw0 >= lk || (causal && kw0 > q0 + BQ - 1));
 
-    // The products start from the row statistics of this lane's query rows
-    // q0 + 8m + 4h + e (register 4m + e of the C layout): S from -LSE/scale,
-    // so that P = exp2(S * scale * log2 e), and dP from -D, so that
-    // dS = P * dP.
-    f32x16 s, dp;
-    {
-      const int64_t roff = (int64_t)hq * p.T_q + sq;
-      const rsrc_t l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
-      const rsrc_t d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
-      const uint32_t off = (uint32_t)(q0 + 4 * h) * 4u;
-      f32x4 lv[4], dv[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        lv[m] = __builtin_bit_cast(f32x4, buf_load16(l_rs, off + 32u * m, 0));
-        dv[m] = __builtin_bit_cast(f32x4, buf_load16(d_rs, off + 32u * m, 0));
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          s[4 * m + e] = lv[m][e];
-          dp[4 * m + e] = dv[m][e];
-        }
-    }
     load_q(hq_n, q0_n, more);
     flush_dq(iter > 0);
 
@@ -466,6 +470,7 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         }
       }
     }
+    load_stats(hq_n, q0_n, more);
     __syncthreads();  // dS complete; every wave is done with this query tile
     if (more) store_q();
 
