@@ -404,16 +404,25 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     flush_dq(iter > 0);
 
     if (active) {
+      // Software pipelined: the operands of step c + 1 are read before the
+      // products of step c, and the scheduler is kept from undoing it.
       const uint32_t a_q = opaque(b_q), a_k = opaque(b_k);
+      u32x4 qa[2], ka[2], oa[2], va[2];
+      auto ld_s = [&](int c, int slot) {
+        const uint32_t cx = (uint32_t)c << 5;
+        qa[slot] = *(const u32x4*)(Qb + (a_q ^ cx));
+        ka[slot] = *(const u32x4*)(Kt + (a_k ^ cx));
+        oa[slot] = *(const u32x4*)(Ob + (a_q ^ cx));
+        va[slot] = *(const u32x4*)(Vt + (a_k ^ cx));
+      };
+      ld_s(0, 0);
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
-        const uint32_t cx = (uint32_t)c << 5;
-        const u32x4 qa = *(const u32x4*)(Qb + (a_q ^ cx));
-        const u32x4 ka = *(const u32x4*)(Kt + (a_k ^ cx));
-        const u32x4 oa = *(const u32x4*)(Ob + (a_q ^ cx));
-        const u32x4 va = *(const u32x4*)(Vt + (a_k ^ cx));
-        s = DT::mfma(as_vec8<DT>(qa), as_vec8<DT>(ka), s);
-        dp = DT::mfma(as_vec8<DT>(oa), as_vec8<DT>(va), dp);
+        if (c + 1 < NC) ld_s(c + 1, (c + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        s = DT::mfma(as_vec8<DT>(qa[c & 1]), as_vec8<DT>(ka[c & 1]), s);
+        dp = DT::mfma(as_vec8<DT>(oa[c & 1]), as_vec8<DT>(va[c & 1]), dp);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // mask: key past lk, query row past lq, or (causal) key after the row
       const bool need_mask = (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0);
@@ -444,17 +453,23 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
       // the order in which P / dS hold them: two transpose reads.
       const uint32_t a_t = opaque(b_t);
+      u32x4 to[2], tq[2];
+      auto ld_t = [&](int i, int slot) {
+        const int dt = i >> 1, kb = i & 1;
+        const uint32_t t0 = a_t ^ tr_xor<DP>(dt, kb, 0);
+        const uint32_t t1 = a_t ^ tr_xor<DP>(dt, kb, 1);
+        to[slot] = cat2(lds_read_tr(Ob, t0), lds_read_tr(Ob, t1));
+        tq[slot] = cat2(lds_read_tr(Qb, t0), lds_read_tr(Qb, t1));
+      };
+      ld_t(0, 0);
 #pragma unroll
-      for (int dt = 0; dt < ND; ++dt) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const uint32_t t0 = a_t ^ tr_xor<DP>(dt, kb, 0);
-          const uint32_t t1 = a_t ^ tr_xor<DP>(dt, kb, 1);
-          const u32x4 to = cat2(lds_read_tr(Ob, t0), lds_read_tr(Ob, t1));
-          const u32x4 tq = cat2(lds_read_tr(Qb, t0), lds_read_tr(Qb, t1));
-          dv_acc[dt] = DT::mfma(as_vec8<DT>(to), pb[kb], dv_acc[dt]);
-          dk_acc[dt] = DT::mfma(as_vec8<DT>(tq), db[kb], dk_acc[dt]);
-        }
+      for (int i = 0; i < 2 * ND; ++i) {
+        const int dt = i >> 1, kb = i & 1;
+        if (i + 1 < 2 * ND) ld_t(i + 1, (i + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dv_acc[dt] = DT::mfma(as_vec8<DT>(to[i & 1]), pb[kb], dv_acc[dt]);
+        dk_acc[dt] = DT::mfma(as_vec8<DT>(tq[i & 1]), db[kb], dk_acc[dt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // dS (query-major) for the dQ product; elements are taken from the
       // packed 32-bit words (element j sits in word j/2, half j&1).
@@ -485,17 +500,30 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       const uint32_t a_d = opaque(b_d), a_kt = opaque(b_kt);
       dq[0] = f32x4_t{};
       dq[1] = f32x4_t{};
-#pragma unroll 2
-      for (int st = 0; st < nst; ++st) {
+      // Software pipelined like the products above.  The read for the step
+      // after the last is clamped to a step inside the tiles (and unused), so
+      // that every iteration has the same reads in flight.
+      u32x4 kt[2], da0[2], da1[2];
+      auto ld_q = [&](int st, int slot) {
         const uint32_t k_x = (uint32_t)(32 * st) * (DP * 2);
-        const uint32_t kt0 = a_kt ^ k_x;
-        const uint32_t kt1 = a_kt ^ (k_x ^ ((uint32_t)(4 * DP * 2) | 16u));
-        const u32x4 kt = cat2(lds_read_tr(Kt, kt0), lds_read_tr(Kt, kt1));
-#pragma unroll
-        for (int qh = 0; qh < 2; ++qh) {
-          const u32x4 da = *(const u32x4*)(dSs + (a_d ^ (((uint32_t)qh << 13) | ((uint32_t)st << 6))));
-          dq[qh] = DT::mfma16(as_vec8<DT>(da), as_vec8<DT>(kt), dq[qh]);
-        }
+        kt[slot] = cat2(lds_read_tr(Kt, a_kt ^ k_x),
+                        lds_read_tr(Kt, a_kt ^ (k_x ^ ((uint32_t)(4 * DP * 2) | 16u))));
+        da0[slot] = *(const u32x4*)(dSs + (a_d ^ ((uint32_t)st << 6)));
+        da1[slot] = *(const u32x4*)(dSs + (a_d ^ ((1u << 13) | ((uint32_t)st << 6))));
+      };
+      ld_q(0, 0);
+      for (int st = 0; st < nst; st += 2) {
+        ld_q(min(st + 1, BK / 32 - 1), 1);
+        __builtin_amdgcn_sched_barrier(0);
+        dq[0] = DT::mfma16(as_vec8<DT>(da0[0]), as_vec8<DT>(kt[0]), dq[0]);
+        dq[1] = DT::mfma16(as_vec8<DT>(da1[0]), as_vec8<DT>(kt[0]), dq[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (st + 1 >= nst) break;
+        ld_q(min(st + 2, BK / 32 - 1), 0);
+        __builtin_amdgcn_sched_barrier(0);
+        dq[0] = DT::mfma16(as_vec8<DT>(da0[1]), as_vec8<DT>(kt[1]), dq[0]);
+        dq[1] = DT::mfma16(as_vec8<DT>(da1[1]), as_vec8<DT>(kt[1]), dq[1]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       hq_p = hq;
       q0_p = q0;
