@@ -406,14 +406,15 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     if (active) {
       // Software pipelined: the operands of step c + 1 are read before the
       // products of step c, and the scheduler is kept from undoing it.
-      const uint32_t a_q = opaque(b_q), a_k = opaque(b_k);
+      // (V lies past the offset field's reach, so it gets its own base.)
+      const uint32_t a_q = opaque(b_q), a_k = opaque(b_k), a_v = opaque(b_k + OFF_V);
       u32x4 qa[2], ka[2], oa[2], va[2];
       auto ld_s = [&](int c, int slot) {
         const uint32_t cx = (uint32_t)c << 5;
         qa[slot] = *(const u32x4*)(Qb + (a_q ^ cx));
         ka[slot] = *(const u32x4*)(Kt + (a_k ^ cx));
         oa[slot] = *(const u32x4*)(Ob + (a_q ^ cx));
-        va[slot] = *(const u32x4*)(Vt + (a_k ^ cx));
+        va[slot] = *(const u32x4*)(smem + (a_v ^ cx));
       };
       ld_s(0, 0);
 #pragma unroll
@@ -424,16 +425,22 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         dp = DT::mfma(as_vec8<DT>(oa[c & 1]), as_vec8<DT>(va[c & 1]), dp);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // mask: key past lk, query row past lq, or (causal) key after the row
+      // mask: key past lk, query row past lq, or (causal) key after the row.
+      // Only tiles on the diagonal or at a sequence's end need it; a masked
+      // score becomes -inf, whose exp2 is 0.
       const bool need_mask = (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0);
-      const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
-      const int row_hi = lq - q0;                  // visible iff qi < lq - q0
-      const bool key_ok = my_k < lk;
+      if (__builtin_expect(need_mask, 0)) {
+        const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
+        const int row_hi = my_k < lk ? lq - q0 : 0;  // visible iff qi < lq - q0
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
+          if (!(qi >= lim_lo && qi < row_hi)) s[i] = -__builtin_inff();
+        }
+      }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-        float pv = __builtin_amdgcn_exp2f(s[i] * c2);
-        if (need_mask) pv = (key_ok && qi >= lim_lo && qi < row_hi) ? pv : 0.f;
+        const float pv = __builtin_amdgcn_exp2f(s[i] * c2);
         s[i] = pv;
         dp[i] = pv * dp[i];
       }
