@@ -342,20 +342,24 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
   int hq_p = hq, q0_p = q0;  // query tile that dq belongs to
   const int dcol = 16 * w + g16;
+  // Atomic j (0..7) adds dq[j / 4][j % 4]: rows past lq fall outside the
+  // resource and are dropped; accumulator layout [h_q][T_q][DP]: the 4 rows
+  // of a lane are immediate offsets.
+  rsrc_t acc_rs;
+  uint32_t acc_base = kOobOffset;
+  auto setup_dq = [&](bool real) {
+    acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq_p * p.T_q + sq) * DP, (uint32_t)lq * (DP * 4));
+    acc_base = (real && dcol < p.d) ? (uint32_t)((q0_p + 4 * grp) * DP + dcol) * 4u : kOobOffset;
+  };
+  auto atomic_dq = [&](int j) {
+    const int qh = j >> 2, e = j & 3;
+    buf_atomic_add(dq[qh][e], acc_rs,
+                   acc_base == kOobOffset ? kOobOffset : acc_base + (16 * qh + e) * DP * 4, 0);
+  };
   auto flush_dq = [&](bool real) {
-    // rows past lq fall outside the resource and are dropped; accumulator
-    // layout [h_q][T_q][DP]: the 4 rows of a lane are immediate offsets
-    const rsrc_t acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq_p * p.T_q + sq) * DP,
-                                    (uint32_t)lq * (DP * 4));
+    setup_dq(real);
 #pragma unroll
-    for (int qh = 0; qh < 2; ++qh) {
-      const uint32_t base = (real && dcol < p.d)
-                                ? (uint32_t)((q0_p + 16 * qh + 4 * grp) * DP + dcol) * 4u
-                                : kOobOffset;
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        buf_atomic_add(dq[qh][e], acc_rs, base == kOobOffset ? kOobOffset : base + e * DP * 4, 0);
-    }
+    for (int j = 0; j < 8; ++j) atomic_dq(j);
   };
 
   // The products start from the row statistics of this lane's query rows
@@ -365,24 +369,32 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   // registers themselves once the previous tile is done with them; the last
   // load goes out of range.
   f32x16 s, dp;
-  auto load_stats = [&](int hq_, int q0_, bool real) {
+  // Load j (0..7): rows 8m + 4h .. +3 (m = j / 2) of -LSE/scale (j even) or
+  // -D (j odd) into S or dP registers 4m .. 4m+3.
+  rsrc_t l_rs, d_rs;
+  uint32_t st_off = kOobOffset;
+  auto setup_stats = [&](int hq_, int q0_, bool real) {
     const int64_t roff = real ? (int64_t)hq_ * p.T_q + sq : 0;
-    const rsrc_t l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
-    const rsrc_t d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
-    const uint32_t off = real ? (uint32_t)(q0_ + 4 * h) * 4u : kOobOffset;
-    f32x4 lv[4], dv[4];
+    l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
+    d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
+    st_off = real ? (uint32_t)(q0_ + 4 * h) * 4u : kOobOffset;
+  };
+  auto load_stat = [&](int j) {
+    const int m = j >> 1;
+    const uint32_t off = st_off == kOobOffset ? kOobOffset : st_off + 32u * m;
+    const f32x4 v = __builtin_bit_cast(f32x4, buf_load16((j & 1) ? d_rs : l_rs, off, 0));
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      lv[m] = __builtin_bit_cast(f32x4, buf_load16(l_rs, real ? off + 32u * m : kOobOffset, 0));
-      dv[m] = __builtin_bit_cast(f32x4, buf_load16(d_rs, real ? off + 32u * m : kOobOffset, 0));
+    for (int e = 0; e < 4; ++e) {
+      if (j & 1)
+        dp[4 * m + e] = v[e];
+      else
+        s[4 * m + e] = v[e];
     }
+  };
+  auto load_stats = [&](int hq_, int q0_, bool real) {
+    setup_stats(hq_, q0_, real);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        s[4 * m + e] = lv[m][e];
-        dp[4 * m + e] = dv[m][e];
-      }
+    for (int j = 0; j < 8; ++j) load_stat(j);
   };
 
   if (n_iter > 0) {
@@ -395,15 +407,19 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     const bool more = iter + 1 < n_iter;
     int hq_n = hq, q0_n = q0;
     advance(hq_n, q0_n);
-    // A wave none of whose keys is visible to this query tile (past lk, or
-    // all after the tile's last row when causal) skips its products: its dS
-    // columns lie beyond the keys the dQ product reads.
-    const bool active = !(kw0 >= lk || (causal && kw0 > q0 + BQ - 1));
 
     load_q(hq_n, q0_n, more);
-    flush_dq(iter > 0);
+    // The previous tile's dQ atomics and the next tile's row statistics are
+    // spread over the product loops below (one or more per step), where they
+    // issue while the matrix cores work.
+    setup_dq(iter > 0);
+    setup_stats(hq_n, q0_n, more);
+    constexpr int kVm = 8 / NC;  // atomics or loads per step (NC = 2 * ND)
 
-    if (active) {
+    // Every wave runs the same path (a wave none of whose keys is visible to
+    // this query tile is masked to zeros), so that all of them issue the same
+    // vector memory operations in the same order and the waits stay exact.
+    {
       // Software pipelined: the operands of step c + 1 are read before the
       // products of step c, and the scheduler is kept from undoing it.
       // (V lies past the offset field's reach, so it gets its own base.)
@@ -423,6 +439,8 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         s = DT::mfma(as_vec8<DT>(qa[c & 1]), as_vec8<DT>(ka[c & 1]), s);
         dp = DT::mfma(as_vec8<DT>(oa[c & 1]), as_vec8<DT>(va[c & 1]), dp);
+#pragma unroll
+        for (int j = 0; j < kVm; ++j) atomic_dq(kVm * c + j);
         __builtin_amdgcn_sched_barrier(0);
       }
       // mask: key past lk, query row past lq, or (causal) key after the row.
@@ -476,6 +494,8 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         __builtin_amdgcn_sched_barrier(0);
         dv_acc[dt] = DT::mfma(as_vec8<DT>(to[i & 1]), pb[kb], dv_acc[dt]);
         dk_acc[dt] = DT::mfma(as_vec8<DT>(tq[i & 1]), db[kb], dk_acc[dt]);
+#pragma unroll
+        for (int j = 0; j < kVm; ++j) load_stat(kVm * i + j);
         __builtin_amdgcn_sched_barrier(0);
       }
       // dS (query-major) for the dQ product; elements are taken from the
@@ -492,7 +512,6 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
         }
       }
     }
-    load_stats(hq_n, q0_n, more);
     __syncthreads();  // dS complete; every wave is done with this query tile
     if (more) store_q();
 
