@@ -6,7 +6,12 @@ the current stream with inputs already resident in HBM.  Workload: 16 causal
 sequences with lengths uniform in [64, 2048] (seed 2, 16,640 tokens), 16
 heads, head_dim 128, bf16, dO ~ N(0,1).
 
-    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--spinup-seconds 1.5]
+                    [--no-cpu-baseline]
+
+Before the W warm-up steps the same step runs untimed for --spinup-seconds:
+the first few hundred milliseconds under load run at lower clocks, which
+would otherwise make the timed steps depend on what ran before them.
 
 Prints one JSON line.  `value` is valid-pair TFLOP/s of fwd+bwd (14*d FLOPs
 per valid (query, key) pair and head); `roofline` describes the dominant
@@ -30,8 +35,9 @@ PEAK_HBM_GBS = 8000.0
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--spinup-seconds", type=float, default=1.5)
     ap.add_argument("--config", default="2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -187,6 +193,21 @@ def main():
                                           P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
                                           ws_bytes, stream, ev_arrays[i]), "bwd")
 
+    def untimed_step():
+        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], stream),
+                   "mask q")
+        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
+                   "mask kv")
+        _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
+                                    fws_bytes, stream), "fwd")
+        _lib.check(lib.thd_attn_bwd(args, P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"],
+                                    P["dq"], P["dk"], P["dv"], P["ws"], ws_bytes, stream), "bwd")
+
+    t_spin = time.perf_counter()
+    while time.perf_counter() - t_spin < a.spinup_seconds:
+        for _ in range(10):
+            untimed_step()
+        torch.cuda.synchronize()
     for i in range(a.warmup):
         step(i)
     torch.cuda.synchronize()
