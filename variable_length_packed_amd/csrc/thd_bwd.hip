@@ -119,36 +119,35 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   if (pair >= p.T_q * p.h_q) return;  // whole 16-lane groups leave together
   const int64_t row = pair / p.h_q;
   const int hh = (int)(pair - row * p.h_q);
-  const bool valid = row_is_valid(p.cu_q, p.pad_q, p.batch, row, p.T_q);
+  // Every row is processed, pad rows included: the main kernel reads -D and
+  // -LSE/scale only at rows inside a sequence (through range-limited
+  // resources), and the accumulator of a pad row receives no atomics, so it
+  // stays zero and converts to the +0 the pad rows of dq need.
   const int64_t off = row * (int64_t)p.h_q * p.d + (int64_t)hh * p.d + 8 * c;
   float acc = 0.f;
   if (8 * c < p.d) {
-    if (valid) {
-      const u32x4 a = *(const u32x4*)(p.o + off);
-      const u32x4 g = *(const u32x4*)(p.dout + off);
+    const u32x4 a = *(const u32x4*)(p.o + off);
+    const u32x4 g = *(const u32x4*)(p.dout + off);
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        acc += DT::to_f32((uint16_t)(a[w] & 0xffffu)) * DT::to_f32((uint16_t)(g[w] & 0xffffu));
-        acc += DT::to_f32((uint16_t)(a[w] >> 16)) * DT::to_f32((uint16_t)(g[w] >> 16));
-      }
+    for (int w = 0; w < 4; ++w) {
+      acc += DT::to_f32((uint16_t)(a[w] & 0xffffu)) * DT::to_f32((uint16_t)(g[w] & 0xffffu));
+      acc += DT::to_f32((uint16_t)(a[w] >> 16)) * DT::to_f32((uint16_t)(g[w] >> 16));
     }
   }
   if (8 * c < DP) {
     // accumulator layout [h_q][T_q][DP]
-    float* acc = p.dq_acc + ((int64_t)hh * p.T_q + row) * DP + 8 * c;
+    float* dst = p.dq_acc + ((int64_t)hh * p.T_q + row) * DP + 8 * c;
     const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)acc = z;
-    *(f32x4*)(acc + 4) = z;
+    *(f32x4*)dst = z;
+    *(f32x4*)(dst + 4) = z;
   }
   acc += __shfl_xor(acc, 8, 16);
   acc += __shfl_xor(acc, 4, 16);
   acc += __shfl_xor(acc, 2, 16);
   acc += __shfl_xor(acc, 1, 16);
-  if (c == 0) p.dsum[(int64_t)hh * p.T_q + row] = valid ? -acc : 0.f;  // -D
-  if (c == 1) {
-    const int64_t i = (int64_t)hh * p.T_q + row;
-    p.lsum[i] = valid ? p.lse[i] * (-1.0f / p.scale) : 0.f;
-  }
+  const int64_t i = (int64_t)hh * p.T_q + row;
+  if (c == 0) p.dsum[i] = -acc;                         // -D
+  if (c == 1) p.lsum[i] = p.lse[i] * (-1.0f / p.scale);  // -LSE / scale
 }
 
 // ---------------------------------------------------------------------------
