@@ -168,7 +168,7 @@ def main():
                                      ws=ws, fws=fws, cu_q=cu_q, cu_kv=cu_kv, mq=mask_q,
                                      mkv=mask_kv).items()}
     import ctypes
-    n_ev = 6
+    n_ev = 7   # 0/1 around the forward, 2..5 the backward passes, 6 the step start
     total = a.warmup + a.steps
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(total)]
     cur = torch.cuda.current_stream(dev)
@@ -181,6 +181,7 @@ def main():
 
     def step(i):
         evs = events[i]
+        evs[6].record(cur)
         _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], stream),
                    "mask q")
         _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
@@ -222,6 +223,8 @@ def main():
     pre_ms = [e[2].elapsed_time(e[3]) for e in timed]
     main_ms = [e[3].elapsed_time(e[4]) for e in timed]
     post_ms = [e[4].elapsed_time(e[5]) for e in timed]
+    mask_ms = [e[6].elapsed_time(e[0]) for e in timed]
+    step_ms = sorted(e[6].elapsed_time(e[5]) for e in timed)
     mean = lambda xs: sum(xs) / len(xs)
 
     pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, w.h_q)
@@ -254,6 +257,10 @@ def main():
         "dtype": "bf16" if w.dtype == "bf16" else "fp16",
         "data": "synthetic",
         "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        # the same time credited with 12*d FLOPs per valid pair (no S recompute)
+        "value_no_recompute_credit": round(value * 12 / 14, 2),
+        "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 4),
+                           "min": round(step_ms[0], 4)},
         "config": {
             "workload": (f"packed thd self-attention, config {w.name}: {w.batch} sequences, "
                          f"{w.T_q} tokens, h_q={w.h_q} h_kv={w.h_kv} d={w.d} {w.dtype}, "
@@ -262,7 +269,8 @@ def main():
             "head_dim": w.d, "valid_pairs": int(pairs), "flops_per_step": int(flops),
             "seed": w.seed,
         },
-        "kernel_ms": {"fwd": round(mean(fwd_ms), 4), "bwd_pre": round(mean(pre_ms), 4),
+        "kernel_ms": {"masks": round(mean(mask_ms), 4),
+                      "fwd": round(mean(fwd_ms), 4), "bwd_pre": round(mean(pre_ms), 4),
                       "bwd_main": round(mean(main_ms), 4), "bwd_post": round(mean(post_ms), 4)},
         "roofline": roofline,
         "cpu_baseline": None,

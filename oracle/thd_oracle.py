@@ -27,7 +27,10 @@ is listed with the design notes of the repository.  In particular:
 
 * softmax scale defaults to 1/sqrt(head_dim) (the only scale that reproduces
   the issue's printed reference output);
-* causal is top-left aligned: query i of a sequence sees key j iff j <= i;
+* ``padding_causal`` is top-left aligned: query i of a sequence sees key j
+  iff j <= i; ``padding_causal_bottom_right`` (the third mask type of the
+  maintainer's ``attn_mask_type_per_seq`` proposal in the per-sequence causal
+  PR) aligns the diagonal with the last key: j <= i + (lk - lq);
 * sequence b occupies rows [start_b, start_b + len_b) where start_b is
   ``cu_seqlens_padded[b]`` when given, else ``cu_seqlens[b]``; every other
   row is pad and every output written for it is 0;
@@ -41,6 +44,9 @@ import math
 import numpy as np
 
 __all__ = [
+    "MASK_PADDING",
+    "MASK_CAUSAL",
+    "MASK_CAUSAL_BOTTOM_RIGHT",
     "padding_mask",
     "padding_mask_loop",
     "sequence_rows",
@@ -50,6 +56,19 @@ __all__ = [
     "attn_bwd",
     "attn_rows",
 ]
+
+
+# Per-sequence mask types ("Add per-sequence causal policy to packed THD
+# attention", maintainer review: a per-sequence mask type naming "padding",
+# "padding_causal" and "padding_causal_bottom_right").  A boolean causal flag
+# is the special case 0 / 1.
+MASK_PADDING = 0
+MASK_CAUSAL = 1
+MASK_CAUSAL_BOTTOM_RIGHT = 2
+
+
+def _mask_type(mask_type, b):
+    return int(mask_type[b]) if mask_type is not None else MASK_PADDING
 
 
 # ---------------------------------------------------------------------------
@@ -121,29 +140,34 @@ def sequence_rows(cu_seqlens, batch_size, cu_seqlens_padded=None):
     return [(starts[b], cu[b + 1] - cu[b]) for b in range(batch_size)]
 
 
-def visible_keys(lq, lk, causal):
+def visible_keys(lq, lk, mask_type):
     """Boolean [lq, lk]: True where query i may attend key j.
 
-    ``padding``: every valid key.  ``padding_causal`` (per-sequence flag of
-    "Add per-sequence causal policy to packed THD attention"): top-left
-    aligned, j <= i.
+    ``padding`` (0): every valid key.  ``padding_causal`` (1, the per-sequence
+    flag of "Add per-sequence causal policy to packed THD attention"):
+    top-left aligned, j <= i.  ``padding_causal_bottom_right`` (2, named in
+    that PR's maintainer review): the diagonal ends at the last key,
+    j <= i + (lk - lq); when lq > lk the first lq - lk queries see no key.
+    Any other value is taken as ``padding``.
     """
     i = np.arange(lq)[:, None]
     j = np.arange(lk)[None, :]
     allowed = np.ones((lq, lk), dtype=bool)
-    if causal:
+    mt = int(mask_type)
+    if mt == MASK_CAUSAL:
         allowed &= j <= i
+    elif mt == MASK_CAUSAL_BOTTOM_RIGHT:
+        allowed &= j <= i + (lk - lq)
     return allowed
 
 
-def valid_pairs(cu_q, cu_kv, batch_size, is_causal=None):
+def valid_pairs(cu_q, cu_kv, batch_size, mask_type=None):
     """Number of (query, key) pairs that attention actually computes, per head."""
     total = 0
     for b in range(batch_size):
         lq = int(cu_q[b + 1]) - int(cu_q[b])
         lk = int(cu_kv[b + 1]) - int(cu_kv[b])
-        c = bool(is_causal[b]) if is_causal is not None else False
-        total += int(visible_keys(lq, lk, c).sum())
+        total += int(visible_keys(lq, lk, _mask_type(mask_type, b)).sum())
     return total
 
 
@@ -166,7 +190,7 @@ def _check_shapes(q, k, v):
 # Forward
 # ---------------------------------------------------------------------------
 
-def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, is_causal=None,
+def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, mask_type=None,
              cu_q_padded=None, cu_kv_padded=None, scale=None):
     """softmax(scale * Q K^T + mask) V, one sequence at a time.
 
@@ -176,8 +200,8 @@ def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, is_causal=None,
     key is 0 / -inf too.
 
     This is the attention of the issue's full reference call, restricted to
-    each sequence's valid tokens, with the per-sequence causal policy and the
-    padded placement of the two-call example.
+    each sequence's valid tokens, with the per-sequence mask type
+    (``visible_keys``) and the padded placement of the two-call example.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -195,10 +219,9 @@ def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, is_causal=None,
     for b in range(batch_size):
         oq, lq = rows_q[b]
         ok, lk = rows_k[b]
-        causal = bool(is_causal[b]) if is_causal is not None else False
         if lq <= 0:
             continue
-        allowed = visible_keys(lq, lk, causal)
+        allowed = visible_keys(lq, lk, _mask_type(mask_type, b))
         for hq in range(h_q):
             hk = hq // group
             Q = q[oq:oq + lq, hq, :]
@@ -222,7 +245,7 @@ def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, is_causal=None,
 # Backward
 # ---------------------------------------------------------------------------
 
-def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, is_causal=None,
+def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, mask_type=None,
              cu_q_padded=None, cu_kv_padded=None, scale=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for ``attn_fwd``.
 
@@ -253,10 +276,9 @@ def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, is_causal=None,
     for b in range(batch_size):
         oq, lq = rows_q[b]
         ok, lk = rows_k[b]
-        causal = bool(is_causal[b]) if is_causal is not None else False
         if lq <= 0 or lk <= 0:
             continue
-        allowed = visible_keys(lq, lk, causal)
+        allowed = visible_keys(lq, lk, _mask_type(mask_type, b))
         has_key = allowed.any(axis=1)
         for hq in range(h_q):
             hk = hq // group
@@ -284,7 +306,7 @@ def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, is_causal=None,
 # Selected rows of one sequence and head (for checks at full size)
 # ---------------------------------------------------------------------------
 
-def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, is_causal=None,
+def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, mask_type=None,
               cu_q_padded=None, cu_kv_padded=None, scale=None):
     """Output, log-sum-exp and dq of chosen query rows of sequence b, head hq.
 
@@ -300,7 +322,7 @@ def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, is_causal=None,
     scale = _default_scale(d, scale)
     (oq, lq), = [sequence_rows(cu_q, b + 1, cu_q_padded)[b]]
     (ok, lk), = [sequence_rows(cu_kv, b + 1, cu_kv_padded)[b]]
-    causal = bool(is_causal[b]) if is_causal is not None else False
+    mt = _mask_type(mask_type, b)
     hk = hq // group
     K = np.asarray(k[ok:ok + lk, hk, :], dtype=np.float64)
     V = np.asarray(v[ok:ok + lk, hk, :], dtype=np.float64)
@@ -309,7 +331,13 @@ def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, is_causal=None,
         if not 0 <= i < lq:
             raise IndexError(i)
         qi = np.asarray(q[oq + i, hq, :], dtype=np.float64)
-        n_vis = min(i + 1, lk) if causal else lk
+        # keys 0 .. n_vis-1 are visible to row i (visible_keys, one row)
+        if mt == MASK_CAUSAL:
+            n_vis = min(i + 1, lk)
+        elif mt == MASK_CAUSAL_BOTTOM_RIGHT:
+            n_vis = min(max(i + 1 + lk - lq, 0), lk)
+        else:
+            n_vis = lk
         if n_vis == 0:
             outs.append(np.zeros(d)); lses.append(-np.inf); dqs.append(np.zeros(d))
             continue

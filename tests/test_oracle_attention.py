@@ -367,3 +367,130 @@ def test_row_sampled_oracle_matches_whole_sequence_oracle():
             np.testing.assert_allclose(o_r, out[s:s + n, hq], atol=1e-13)
             np.testing.assert_allclose(l_r, lse[hq, s:s + n], atol=1e-13)
             np.testing.assert_allclose(dq_r, dq[s:s + n, hq], atol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Bottom-right causal alignment (the third per-sequence mask type of the
+# maintainer's proposal in "Add per-sequence causal policy to packed THD
+# attention"): each case reduces to the top-left or full attention above.
+# ---------------------------------------------------------------------------
+
+def _one_seq(q, k, v, do, mt):
+    cq = np.array([0, q.shape[0]], np.int32)
+    ck = np.array([0, k.shape[0]], np.int32)
+    out, lse = attn_fwd(q, k, v, cq, ck, 1, [mt])
+    grads = attn_bwd(q, k, v, do, cq, ck, 1, [mt])
+    return out, lse, grads
+
+
+@pytest.mark.parametrize("lq,lk", [(5, 9), (1, 7), (3, 3)])
+def test_bottom_right_is_top_left_with_queries_prepended(lq, lk):
+    # lk >= lq: query i sees keys 0 .. i + lk - lq, which is what query
+    # i + lk - lq sees under top-left alignment when lk - lq extra queries
+    # come first.  Extra queries get dO = 0, so dK and dV agree as well.
+    rng = np.random.default_rng(lq * 31 + lk)
+    q = rng.standard_normal((lq, 2, 8))
+    extra = rng.standard_normal((lk - lq, 2, 8))
+    k = rng.standard_normal((lk, 1, 8))
+    v = rng.standard_normal((lk, 1, 8))
+    do = rng.standard_normal((lq, 2, 8))
+    out, lse, (dq, dk, dv) = _one_seq(q, k, v, do, 2)
+    qx = np.concatenate([extra, q])
+    dox = np.concatenate([np.zeros_like(extra), do])
+    out_t, lse_t, (dq_t, dk_t, dv_t) = _one_seq(qx, k, v, dox, 1)
+    np.testing.assert_allclose(out, out_t[lk - lq:], atol=1e-13)
+    np.testing.assert_allclose(lse, lse_t[:, lk - lq:], atol=1e-13)
+    np.testing.assert_allclose(dq, dq_t[lk - lq:], atol=1e-13)
+    np.testing.assert_allclose(dk, dk_t, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_t, atol=1e-13)
+
+
+@pytest.mark.parametrize("lq,lk", [(9, 5), (4, 1)])
+def test_bottom_right_with_more_queries_than_keys(lq, lk):
+    # lq > lk: the first lq - lk queries see no key (output 0, log-sum-exp
+    # -inf, no gradient); the rest are the top-left causal attention of the
+    # last lk queries.
+    rng = np.random.default_rng(lq * 7 + lk)
+    q = rng.standard_normal((lq, 2, 8))
+    k = rng.standard_normal((lk, 2, 8))
+    v = rng.standard_normal((lk, 2, 8))
+    do = rng.standard_normal((lq, 2, 8))
+    out, lse, (dq, dk, dv) = _one_seq(q, k, v, do, 2)
+    n0 = lq - lk
+    assert not out[:n0].any() and not dq[:n0].any()
+    assert np.all(np.isneginf(lse[:, :n0]))
+    out_t, lse_t, (dq_t, dk_t, dv_t) = _one_seq(q[n0:], k, v, do[n0:], 1)
+    np.testing.assert_allclose(out[n0:], out_t, atol=1e-13)
+    np.testing.assert_allclose(lse[:, n0:], lse_t, atol=1e-13)
+    np.testing.assert_allclose(dq[n0:], dq_t, atol=1e-13)
+    np.testing.assert_allclose(dk, dk_t, atol=1e-13)
+    np.testing.assert_allclose(dv, dv_t, atol=1e-13)
+
+
+def test_bottom_right_single_query_sees_every_key():
+    # one query against a long kv sequence (the decode shape): bottom-right
+    # causal leaves every key visible, so it equals `padding`, while top-left
+    # causal would show it only key 0.
+    rng = np.random.default_rng(3)
+    q = rng.standard_normal((1, 1, 8))
+    k = rng.standard_normal((6, 1, 8))
+    v = rng.standard_normal((6, 1, 8))
+    do = rng.standard_normal((1, 1, 8))
+    br = _one_seq(q, k, v, do, 2)
+    full = _one_seq(q, k, v, do, 0)
+    tl = _one_seq(q, k, v, do, 1)
+    np.testing.assert_allclose(br[0], full[0], atol=1e-14)
+    for a, b in zip(br[2], full[2]):
+        np.testing.assert_allclose(a, b, atol=1e-14)
+    np.testing.assert_allclose(tl[0][0, 0], v[0, 0], atol=1e-14)
+
+
+def test_bottom_right_visible_counts_and_rows():
+    from oracle import attn_rows, visible_keys
+    # counts: row i sees min(max(i + 1 + lk - lq, 0), lk) keys
+    for lq, lk in [(3, 8), (8, 3), (5, 5), (0, 4), (4, 0)]:
+        vk = visible_keys(lq, lk, 2)
+        for i in range(lq):
+            assert vk[i].sum() == min(max(i + 1 + lk - lq, 0), lk)
+            assert not vk[i, vk[i].sum():].any()
+    # the row sampler agrees with the whole-sequence oracle on mixed types
+    w = workloads.random_layout(77, batch=5, max_len=12, h_q=2, h_kv=1, d=8,
+                                dtype="bf16", causal="types", cross=True, min_len=0)
+    assert 2 in w.causal
+    q, k, v, do = (f64(t) for t in workloads.make_tensors(w))
+    out, lse = attn_fwd(q, k, v, w.cu_q, w.cu_kv, w.batch, w.causal)
+    dq, _, _ = attn_bwd(q, k, v, do, w.cu_q, w.cu_kv, w.batch, w.causal)
+    for b, (s, n) in enumerate(sequence_rows(w.cu_q, w.batch)):
+        if n == 0:
+            continue
+        for hq in range(w.h_q):
+            o_r, l_r, dq_r = attn_rows(q, k, v, do, w.cu_q, w.cu_kv, b, hq, list(range(n)),
+                                       w.causal)
+            np.testing.assert_allclose(o_r, out[s:s + n, hq], atol=1e-13)
+            np.testing.assert_allclose(l_r, lse[hq, s:s + n], atol=1e-13)
+            np.testing.assert_allclose(dq_r, dq[s:s + n, hq], atol=1e-13)
+
+
+@pytest.mark.parametrize("seed", [23, 24])
+def test_bottom_right_backward_central_differences(seed):
+    w = workloads.random_layout(seed, batch=3, max_len=5, h_q=2, h_kv=1, d=4,
+                                dtype="fp16", causal="types", cross=True, min_len=1)
+    q, k, v, do = (f64(t) for t in workloads.make_tensors(w))
+    args = (w.cu_q, w.cu_kv, w.batch, np.full(w.batch, 2, np.uint8))
+
+    def loss(qq, kk, vv):
+        o, _ = attn_fwd(qq, kk, vv, *args)
+        return float((o * do).sum())
+
+    grads = attn_bwd(q, k, v, do, *args)
+    eps = 1e-6
+    for idx, (x, g) in enumerate(zip((q, k, v), grads)):
+        num = np.zeros_like(x)
+        for pos in np.ndindex(x.shape):
+            xp = x.copy(); xp[pos] += eps
+            xm = x.copy(); xm[pos] -= eps
+            ins_p = [q, k, v]; ins_p[idx] = xp
+            ins_m = [q, k, v]; ins_m[idx] = xm
+            num[pos] = (loss(*ins_p) - loss(*ins_m)) / (2 * eps)
+        err = np.linalg.norm(num - g) / max(np.linalg.norm(g), 1e-30)
+        assert err < 1e-7, (idx, err)

@@ -46,7 +46,8 @@ class Workload:
     d: int
     lens_q: np.ndarray               # int64 [B]
     lens_kv: np.ndarray              # int64 [B]
-    causal: np.ndarray               # uint8 [B]
+    causal: np.ndarray               # uint8 [B] mask type: 0 padding, 1 top-left
+                                     # causal, 2 bottom-right causal
     cu_q: np.ndarray                 # int32, >= B+1 entries
     cu_kv: np.ndarray                # int32, >= B+1 entries
     cu_q_padded: Optional[np.ndarray] = None
@@ -192,6 +193,8 @@ def random_layout(seed, batch, max_len, *, h_q=2, h_kv=None, d=64,
     lk = rng.integers(min_len, max_len, size=batch, endpoint=True) if cross else None
     if causal == "mixed":
         flags = (rng.random(batch) < 0.5).astype(np.uint8)
+    elif causal == "types":  # all three mask types
+        flags = rng.integers(0, 2, size=batch, endpoint=True).astype(np.uint8)
     elif causal in ("all", True):
         flags = np.ones(batch, np.uint8)
     else:
