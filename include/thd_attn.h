@@ -28,7 +28,7 @@
  *     host or synchronises, so every call may be captured in a HIP graph.
  *   - Only host-visible arguments are validated; an invalid one returns a
  *     negative status before anything is launched.  Device metadata
- *     (cu_seqlens*, is_causal) is never validated: for malformed values every
+ *     (cu_seqlens*, mask_type) is never validated: for malformed values every
  *     row index is clamped into range, so the kernels stay memory-safe, but
  *     the result is unspecified.
  *   - No C++ exception crosses this interface.
@@ -42,11 +42,17 @@
  *   last -- is a pad row: it is never read for attention and every output
  *   written for it is +0.0 (bit pattern 0).
  *
- * Mask [C]
+ * Mask [C] (Description; maintainer review: one mask type per sequence)
  *   Query i of sequence b (0-based inside the sequence) attends key j iff
- *   j < lk_b and (is_causal[b] == 0 or j <= i): "padding" or top-left aligned
- *   "padding_causal".  A query row with no visible key (lk_b == 0) gets
- *   output 0 and log-sum-exp -inf, and has zero gradient.
+ *   j < lk_b and, by mask_type[b]:
+ *     THD_MASK_PADDING (0)                 every such key;
+ *     THD_MASK_CAUSAL (1)                  j <= i ("padding_causal", top-left);
+ *     THD_MASK_CAUSAL_BOTTOM_RIGHT (2)     j <= i + lk_b - lq_b
+ *                                          ("padding_causal_bottom_right");
+ *   any other value is taken as THD_MASK_PADDING, and a 0/1 causal flag per
+ *   sequence is a valid mask_type array.  A query row with no visible key
+ *   (lk_b == 0, or the first lq_b - lk_b rows under bottom-right alignment)
+ *   gets output 0 and log-sum-exp -inf, and has zero gradient.
  *
  * Head mapping: query head hq reads key/value head hq / (h_q / h_kv).
  */
@@ -71,6 +77,12 @@ typedef enum {
 
 typedef enum { THD_FP16 = 0, THD_BF16 = 1 } thd_dtype;
 
+typedef enum {
+  THD_MASK_PADDING = 0,
+  THD_MASK_CAUSAL = 1,
+  THD_MASK_CAUSAL_BOTTOM_RIGHT = 2
+} thd_mask_type;
+
 /* Problem description shared by the attention entry points.  The pointers
  * are DEVICE pointers to int32/uint8 metadata and are read only by kernels. */
 typedef struct {
@@ -78,7 +90,7 @@ typedef struct {
   const int32_t* cu_seqlens_kv;        /* self attention: may alias cu_seqlens_q   */
   const int32_t* cu_seqlens_q_padded;  /* NULL => row starts are cu_seqlens_q      */
   const int32_t* cu_seqlens_kv_padded; /* NULL => row starts are cu_seqlens_kv     */
-  const uint8_t* is_causal;            /* [batch], nonzero = causal; NULL => none  */
+  const uint8_t* mask_type;            /* [batch] thd_mask_type; NULL => padding   */
   int32_t batch;                       /* >= 0; 0 writes zeros everywhere          */
   int32_t max_seqlen_q;                /* >= 0; bound on lq_b (host scalar, [I])   */
   int32_t max_seqlen_kv;               /* >= 0; bound on lk_b                      */

@@ -65,6 +65,13 @@ SMALL = [
          min_len=127),
     dict(seed=108, batch=4, max_len=520, h_q=8, h_kv=2, d=128, dtype="bf16", causal="mixed",
          slot_multiple=64, gap_before=3, min_len=1),
+    # every mask type, bottom-right included, with lq above and below lk
+    dict(seed=111, batch=7, max_len=330, h_q=2, d=128, dtype="bf16", causal="types",
+         cross=True),
+    dict(seed=112, batch=6, max_len=420, h_q=4, h_kv=2, d=64, dtype="fp16", causal="types",
+         cross=True, slot_multiple=64, gap_before=2),
+    dict(seed=113, batch=8, max_len=140, h_q=2, d=32, dtype="bf16", causal="types",
+         cross=True, extra_cu=2, min_len=0),
 ]
 
 
@@ -73,6 +80,21 @@ def test_small_layouts(kw):
     kw = dict(kw)
     seed = kw.pop("seed")
     w = workloads.random_layout(seed, **kw)
+    run_case(w)
+
+
+@pytest.mark.parametrize("more_queries", [False, True])
+def test_bottom_right_chunk_shapes(more_queries):
+    # bottom-right causal on every sequence: query chunks shorter than their
+    # key history (the chunked-prefill shape), or longer (the first lq - lk
+    # rows see no key: output 0, log-sum-exp -inf, zero gradient)
+    rng = np.random.default_rng(120 + more_queries)
+    lq = rng.integers(1, 400, size=6, endpoint=True)
+    extra = rng.integers(0, 700, size=6, endpoint=True)
+    lk = np.maximum(lq - extra, 0) if more_queries else lq + extra
+    w = workloads.packed(lq, lk, causal=np.full(6, 2, np.uint8), h_q=4, h_kv=2, d=128,
+                         dtype="bf16", seed=130 + more_queries,
+                         name=f"br{'_more_q' if more_queries else ''}")
     run_case(w)
 
 

@@ -26,3 +26,16 @@ def test_pad_rows_and_layout():
     assert not valid[:2].any()
     assert (q[~valid].float() == 100).all() and (do[~valid].float() == 100).all()
     assert valid.sum() == w.lens_q.sum()
+
+
+def test_valid_pair_accounting_matches_oracle_masks():
+    # the benchmark's pair count (host arithmetic) against the oracle's masks,
+    # for every mask type and both lq <= lk and lq > lk
+    from oracle import visible_keys
+    from variable_length_packed_amd.metrics import valid_pairs as host_pairs
+    rng = np.random.default_rng(9)
+    lq = rng.integers(0, 40, size=60)
+    lk = rng.integers(0, 40, size=60)
+    mt = rng.integers(0, 4, size=60).astype(np.uint8)
+    expect = sum(int(visible_keys(a, b, t).sum()) for a, b, t in zip(lq, lk, mt))
+    assert host_pairs(lq, lk, mt, h_q=3) == 3 * expect

@@ -4,9 +4,13 @@ The compute path is libthdattn.so (hand-written HIP kernels behind the C ABI
 of include/thd_attn.h); this package is its thin torch binding.
 """
 from .attention import (  # noqa: F401
+    MASK_CAUSAL,
+    MASK_CAUSAL_BOTTOM_RIGHT,
+    MASK_PADDING,
     attn_bwd,
     attn_fwd,
     bwd_workspace_size,
+    fwd_workspace_size,
     padding_mask,
     thd_attention,
 )

@@ -43,7 +43,7 @@ class ThdVarlenArgs(ctypes.Structure):
         ("cu_seqlens_kv", ctypes.c_void_p),
         ("cu_seqlens_q_padded", ctypes.c_void_p),
         ("cu_seqlens_kv_padded", ctypes.c_void_p),
-        ("is_causal", ctypes.c_void_p),
+        ("mask_type", ctypes.c_void_p),
         ("batch", ctypes.c_int32),
         ("max_seqlen_q", ctypes.c_int32),
         ("max_seqlen_kv", ctypes.c_int32),

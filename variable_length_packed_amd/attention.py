@@ -88,15 +88,15 @@ def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
         if t is not None and t.numel() < batch_size + (0 if "padded" in name else 1):
             raise ValueError(f"{name} is shorter than the batch")
     if is_causal is not None:
-        _require_cuda("is_causal", is_causal, (torch.bool, torch.uint8))
+        _require_cuda("mask_type", is_causal, (torch.bool, torch.uint8))
         if is_causal.numel() < batch_size:
-            raise ValueError("is_causal needs one entry per sequence")
+            raise ValueError("mask_type / is_causal needs one entry per sequence")
     a = _lib.ThdVarlenArgs()
     a.cu_seqlens_q = _ptr(cu_q)
     a.cu_seqlens_kv = _ptr(cu_kv)
     a.cu_seqlens_q_padded = _ptr(cu_q_pad)
     a.cu_seqlens_kv_padded = _ptr(cu_kv_pad)
-    a.is_causal = _ptr(is_causal)
+    a.mask_type = _ptr(is_causal)
     a.batch = batch_size
     a.max_seqlen_q = int(max_q)
     a.max_seqlen_kv = int(max_kv)
@@ -110,17 +110,29 @@ def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
     return a
 
 
+def _mask_arg(is_causal, mask_type):
+    if mask_type is not None:
+        if is_causal is not None:
+            raise ValueError("give mask_type or is_causal, not both")
+        return mask_type
+    return is_causal
+
+
 def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, *,
              cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None, is_causal=None,
-             softmax_scale=None, batch_size=None, out=None, lse=None, workspace=None):
+             softmax_scale=None, batch_size=None, out=None, lse=None, workspace=None,
+             mask_type=None):
     """Forward attention; returns (out [T_q,h_q,d], lse [h_q,T_q] fp32).
 
-    ``is_causal``: one bool/uint8 per sequence (None = all ``padding``).
+    ``mask_type``: one uint8 per sequence, MASK_PADDING / MASK_CAUSAL (top-left) /
+    MASK_CAUSAL_BOTTOM_RIGHT (None = all ``padding``); ``is_causal`` (one
+    bool/uint8 per sequence) is the same argument under its older name.
     ``softmax_scale``: None = 1/sqrt(head_dim).  ``batch_size``: number of
     sequences when the cu_seqlens buffers are longer than batch + 1.
     ``workspace``: uint8 device buffer of at least ``fwd_workspace_size``
     bytes (allocated here when None).
     """
+    is_causal = _mask_arg(is_causal, mask_type)
     a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                    cu_seqlens_q_padded, cu_seqlens_kv_padded, is_causal, softmax_scale,
                    batch_size)
@@ -159,8 +171,9 @@ def bwd_workspace_size(q, k, cu_seqlens_q, cu_seqlens_kv, batch_size=None):
 def attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
              max_seqlen_kv, *, cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None,
              is_causal=None, softmax_scale=None, batch_size=None, workspace=None,
-             dq=None, dk=None, dv=None):
-    """Backward attention; returns (dq, dk, dv)."""
+             dq=None, dk=None, dv=None, mask_type=None):
+    """Backward attention; returns (dq, dk, dv).  Arguments as ``attn_fwd``."""
+    is_causal = _mask_arg(is_causal, mask_type)
     a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                    cu_seqlens_q_padded, cu_seqlens_kv_padded, is_causal, softmax_scale,
                    batch_size)
@@ -207,11 +220,16 @@ class _ThdAttention(torch.autograd.Function):
 
 def thd_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, *,
                   cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None, is_causal=None,
-                  softmax_scale=None, batch_size=None):
+                  softmax_scale=None, batch_size=None, mask_type=None):
     """Autograd-enabled packed-thd attention (forward and backward in HIP)."""
     return _ThdAttention.apply(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
                                max_seqlen_kv, cu_seqlens_q_padded, cu_seqlens_kv_padded,
-                               is_causal, softmax_scale, batch_size)
+                               _mask_arg(is_causal, mask_type), softmax_scale, batch_size)
+
+
+MASK_PADDING = 0
+MASK_CAUSAL = 1
+MASK_CAUSAL_BOTTOM_RIGHT = 2
 
 
 def default_scale(head_dim):

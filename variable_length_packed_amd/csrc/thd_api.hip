@@ -36,7 +36,7 @@ int to_problem(const thd_varlen_args* a, thd::Problem* p) {
   p->cu_kv = a->cu_seqlens_kv;
   p->pad_q = a->cu_seqlens_q_padded;
   p->pad_kv = a->cu_seqlens_kv_padded;
-  p->causal = a->is_causal;
+  p->causal = a->mask_type;
   p->batch = a->batch;
   p->T_q = a->total_q;
   p->T_kv = a->total_kv;

@@ -64,13 +64,15 @@ struct BwdParams {
 // ---------------------------------------------------------------------------
 // pre: -D = -rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
 // ---------------------------------------------------------------------------
-// Schedule of the main kernel (largest first, see build_schedule): tile kt
-// of sequence b walks W = ceil(lq / BQ) query tiles, or max(W - kt * BK/BQ, 0)
-// when b is causal (its first query tile is the diagonal one).  Summary:
-// x = ceil(lq / BQ), y = ceil(lk / BK), with the main kernel's clamping.
-constexpr int kStepQ = kBwdBK / kBwdBQ;  // query tiles per key tile
+// Schedule of the main kernel (largest first, see build_schedule): key tile
+// kt of sequence b walks W = ceil(lq / BQ) query tiles, or, with a causal
+// mask type, those from the first one that sees key kt * BK:
+// W = clamp(ceil(lq / BQ) - 8 kt + ceil(off / BQ), 0, ceil(lq / BQ))
+// (BK = 8 BQ), with the main kernel's clamping of the lengths.
+static_assert(kBwdBK == 8 * kBwdBQ, "work model assumes eight query tiles per key tile");
 
 struct BwdSchedModel {
+  static constexpr int kSlope = -8;
   const BwdParams& p;
   __device__ SeqSummary seq(int b) const {
     const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
@@ -79,31 +81,13 @@ struct BwdSchedModel {
         clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 4);
     const int lk =
         clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
+    const int mt = mask_type_of(p.causal, b);
     SeqSummary s;
-    s.x = ceil_div_pos(lq, kBwdBQ);
-    s.y = ceil_div_pos(lk, kBwdBK);
-    s.causal = p.causal ? (p.causal[b] != 0) : false;
+    s.x = ceil_div_pos(lk, kBwdBK);
+    s.H = ceil_div_pos(lq, kBwdBQ);
+    s.causal = mask_is_causal(mt);
+    s.c = s.H + ceil_div(causal_offset(mt, lq, lk), kBwdBQ);
     return s;
-  }
-  static __device__ int items(const SeqSummary& s) { return s.y; }
-  static __device__ int work(const SeqSummary& s, int t) {
-    return s.causal ? max(s.x - kStepQ * t, 0) : s.x;
-  }
-  static __device__ int gt(const SeqSummary& s, int w) {
-    if (!s.causal) return s.x > w ? s.y : 0;
-    return min(ceil_div_pos(s.x - w, kStepQ), s.y);
-  }
-  static __device__ int eq(const SeqSummary& s, int w) {
-    if (!s.causal) return s.x == w ? s.y : 0;
-    if (w > 0) {
-      const int d = s.x - w;
-      return (d >= 0 && d % kStepQ == 0 && d / kStepQ < s.y) ? 1 : 0;
-    }
-    return s.y - min(s.y, ceil_div_pos(s.x, kStepQ));  // tiles with nothing to walk
-  }
-  static __device__ int before(const SeqSummary& s, int t, int w) {
-    if (!s.causal) return t;
-    return w > 0 ? 0 : t - min(t, ceil_div_pos(s.x, kStepQ));
   }
 };
 
@@ -250,7 +234,9 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
   const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
   const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const bool causal = p.causal ? (p.causal[b] != 0) : false;
+  const int mtype = mask_type_of(p.causal, b);
+  const bool causal = mask_is_causal(mtype);
+  const int off = causal_offset(mtype, lq, lk);  // key j visible to query i iff j <= i + off
   const int k0 = tile_in_seq * BK;
   if (k0 >= lk) return;
   const int kw0 = k0 + 32 * w;
@@ -274,8 +260,9 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     }
   }
 
-  // Query tiles: from the first tile that can see key k0 when causal.
-  const int q_start = causal ? (k0 / BQ) * BQ : 0;
+  // Query tiles: from the first tile that can see key k0 when causal
+  // (query k0 - off).
+  const int q_start = causal ? max(floor_div(k0 - off, BQ), 0) * BQ : 0;
   const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
   const int n_iter = p.group * n_qt;
 
@@ -445,9 +432,10 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       // mask: key past lk, query row past lq, or (causal) key after the row.
       // Only tiles on the diagonal or at a sequence's end need it; a masked
       // score becomes -inf, whose exp2 is 0.
-      const bool need_mask = (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0);
+      const bool need_mask =
+          (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0 + off);
       if (__builtin_expect(need_mask, 0)) {
-        const int lim_lo = causal ? my_k - q0 : -1;  // visible iff qi >= my_k - q0
+        const int lim_lo = causal ? my_k - q0 - off : -1;  // visible iff qi >= my_k - off - q0
         const int row_hi = my_k < lk ? lq - q0 : 0;  // visible iff qi < lq - q0
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -520,7 +508,7 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
       // B lane l = K[32s + 8(l/16) + j][16w + l%16] (two transpose reads).
       int kv_act = lk - k0;
       if (kv_act > BK) kv_act = BK;
-      if (causal && q0 + BQ - k0 < kv_act) kv_act = q0 + BQ - k0;
+      if (causal && q0 + BQ + off - k0 < kv_act) kv_act = q0 + BQ + off - k0;
       const int nst = (kv_act + 31) / 32;
       const uint32_t a_d = opaque(b_d), a_kt = opaque(b_kt);
       dq[0] = f32x4_t{};

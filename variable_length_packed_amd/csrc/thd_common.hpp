@@ -199,62 +199,116 @@ __device__ __forceinline__ bool row_is_valid(const int32_t* cu, const int32_t* c
 }
 
 // ---------------------------------------------------------------------------
+// Per-sequence mask types (one uint8 per sequence): key j of a sequence is
+// visible to its query i when j < lk and, for the causal types, j <= i + off
+// with off = 0 (top-left) or lk - lq (bottom-right).  Other values: padding.
+// ---------------------------------------------------------------------------
+constexpr int kMaskPadding = 0;
+constexpr int kMaskCausal = 1;
+constexpr int kMaskCausalBottomRight = 2;
+
+__device__ __forceinline__ int mask_type_of(const uint8_t* types, int b) {
+  return types ? (int)types[b] : kMaskPadding;
+}
+__device__ __forceinline__ bool mask_is_causal(int mt) {
+  return mt == kMaskCausal || mt == kMaskCausalBottomRight;
+}
+__device__ __forceinline__ int causal_offset(int mt, int lq, int lk) {
+  return mt == kMaskCausalBottomRight ? lk - lq : 0;
+}
+
+__device__ __forceinline__ int floor_div(int a, int b) {  // b > 0
+  const int q = a / b;
+  return (a % b != 0 && a < 0) ? q - 1 : q;
+}
+__device__ __forceinline__ int ceil_div(int a, int b) {  // b > 0
+  const int q = a / b;
+  return (a % b != 0 && a > 0) ? q + 1 : q;
+}
+__device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + b - 1) / b : 0; }
+__device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
+
+// ---------------------------------------------------------------------------
 // Largest-first schedules.  The tiles (sequence b, tile t) of a kernel are
 // ranked by their work W, largest first, ties in (b, t) order, and rank r is
 // run by the workgroups r * heads .. r * heads + heads - 1, so the longest
 // workgroups start first and the short ones fill in behind them (greedy list
 // scheduling in decreasing order).  A rank is a count,
 //   rank = #{tiles with larger W} + #{equal W, earlier (b, t)},
-// and a Model gives each sequence's share of both counts in closed form from
-// a summary of the sequence, so no sort is needed:
-//   md.seq(b)          summary {x, y, causal} of sequence b
-//   Model::items(s)    number of tiles of the sequence
-//   Model::work(s, t)  W of tile t
-//   Model::gt(s, w)    #{t : W(t) > w}
-//   Model::eq(s, w)    #{t : W(t) == w}
-//   Model::before(s, t, w)  #{t' < t : W(t') == w}
+// and each sequence's share of both counts has a closed form: a sequence has
+// x tiles, and W(t) = H for all of them (no causal mask) or
+// W(t) = clamp(a t + c, 0, H) with the model's slope a (causal).  A Model
+// gives md.seq(b) = {x, c, H, causal} and kSlope.
 // Output: sched[0] = number of tiles kept (at most cap), then (b, t) of rank
 // r at sched[2 + 2r], sched[3 + 2r].  One wave per sequence (wave_id = b);
 // its lanes take t = lane, lane + 64, ...; the wave of sequence 0 also
 // writes sched[0].
 // ---------------------------------------------------------------------------
 struct SeqSummary {
-  int x, y;  // model-defined tile counts, y < 2^30
+  int x;        // tiles of the sequence
+  int c, H;     // W(t) = clamp(a t + c, 0, H) when causal, else H; H < 2^30
   bool causal;
+};
+
+// #{t in [0, x) : clamp(a t + c, 0, H) > w} for w >= 0, a != 0
+__device__ __forceinline__ int count_gt_lin(int x, int a, int c, int H, int w) {
+  if (x <= 0 || H <= w) return 0;
+  // with H > w >= 0 the clamp keeps W(t) > w exactly when a t + c > w
+  if (a > 0) return x - clampi(floor_div(w - c, a) + 1, 0, x);
+  return clampi(ceil_div(c - w, -a), 0, x);
+}
+__device__ __forceinline__ int count_ge_lin(int x, int a, int c, int H, int w) {
+  return w <= 0 ? x : count_gt_lin(x, a, c, H, w - 1);
+}
+
+template <class Model>
+struct SchedCounts {
+  static __device__ int work(const SeqSummary& s, int t) {
+    return s.causal ? clampi(Model::kSlope * t + s.c, 0, s.H) : s.H;
+  }
+  static __device__ int gt(const SeqSummary& s, int w) {
+    if (!s.causal) return s.H > w ? s.x : 0;
+    return count_gt_lin(s.x, Model::kSlope, s.c, s.H, w);
+  }
+  static __device__ int eq_below(const SeqSummary& s, int n, int w) {  // among t < n
+    if (!s.causal) return s.H == w ? n : 0;
+    return count_ge_lin(n, Model::kSlope, s.c, s.H, w) - count_gt_lin(n, Model::kSlope, s.c, s.H, w);
+  }
 };
 
 template <class Model>
 __device__ void build_schedule(const Model& md, int batch, int cap, int32_t* sched, int wave_id) {
+  typedef SchedCounts<Model> C;
   const int lane = lane_id();
   const int b = uniform(wave_id);
   if (b >= batch) return;
   const SeqSummary sb = md.seq(b);
-  const int nb = Model::items(sb);
   const bool counter = b == 0;
-  int rounds = (nb + 63) / 64;
+  int rounds = (sb.x + 63) / 64;
   if (counter && rounds == 0) rounds = 1;
   for (int rd = 0; rd < rounds; ++rd) {
     const int t = 64 * rd + lane;
-    const int w = Model::work(sb, t);  // unused when t >= nb
-    int64_t rank = Model::before(sb, t, w);
+    const int w = C::work(sb, t);  // unused when t >= x
+    int64_t rank = C::eq_below(sb, t < sb.x ? t : 0, w);
     int64_t total = 0;
     for (int c0 = 0; c0 < batch; c0 += 64) {
       // lane j summarises sequence c0 + j; every lane then visits all of them
-      SeqSummary sj = {0, 0, false};
+      SeqSummary sj = {0, 0, 0, false};
       if (c0 + lane < batch) sj = md.seq(c0 + lane);
-      const int px = sj.x, py = (sj.y << 1) | (sj.causal ? 1 : 0);
+      const int px = sj.x, pc = sj.c, ph = (sj.H << 1) | (sj.causal ? 1 : 0);
       const int n = min(64, batch - c0);
       for (int j = 0; j < n; ++j) {
         SeqSummary o;
         o.x = __builtin_amdgcn_readlane(px, j);
-        const int y = __builtin_amdgcn_readlane(py, j);
-        o.y = y >> 1;
-        o.causal = (y & 1) != 0;
-        rank += Model::gt(o, w) + (c0 + j < b ? Model::eq(o, w) : 0);
-        total += Model::items(o);
+        o.c = __builtin_amdgcn_readlane(pc, j);
+        const int hv = __builtin_amdgcn_readlane(ph, j);
+        o.H = hv >> 1;
+        o.causal = (hv & 1) != 0;
+        rank += C::gt(o, w) + (c0 + j < b ? C::eq_below(o, o.x, w) : 0);
+        total += o.x;
       }
     }
-    if (t < nb && rank < cap) {  // ranks are a permutation of [0, total)
+    if (t < sb.x && rank < cap) {  // ranks are a permutation of [0, total)
       int2 e;
       e.x = b;
       e.y = t;
@@ -263,7 +317,5 @@ __device__ void build_schedule(const Model& md, int batch, int cap, int32_t* sch
     if (counter && rd == 0 && lane == 0) sched[0] = (int)min(total, (int64_t)cap);
   }
 }
-
-__device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + b - 1) / b : 0; }
 
 }  // namespace thd

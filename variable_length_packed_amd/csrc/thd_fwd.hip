@@ -51,12 +51,14 @@ struct FwdParams {
 };
 
 // Schedule of the attention workgroups (largest first, see build_schedule):
-// query tile t of sequence b walks W = ceil(lk / BN) key tiles, or
-// min(W, 2t + 2) when b is causal (keys up to the tile's last row, BM = 2 BN).
-// Summary: x = ceil(lq / BM), y = ceil(lk / BN), with the kernel's clamping.
+// query tile t of sequence b walks W = ceil(lk / BN) key tiles, or, with a
+// causal mask type, the tiles up to its last row's diagonal:
+// W = ceil(clamp(min(lk, (t + 1) BM + off), 0) / BN) = clamp(2t + 2 + ceil(off / BN), 0, ceil(lk / BN))
+// (BM = 2 BN), with the kernel's clamping of the lengths.
 static_assert(kFwdBM == 2 * kFwdBN, "work model assumes two key tiles per query tile");
 
 struct FwdSchedModel {
+  static constexpr int kSlope = 2;
   const FwdParams& p;
   __device__ SeqSummary seq(int b) const {
     const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
@@ -65,30 +67,13 @@ struct FwdSchedModel {
         clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 2);
     const int lk =
         clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
+    const int mt = mask_type_of(p.causal, b);
     SeqSummary s;
     s.x = ceil_div_pos(lq, kFwdBM);
-    s.y = ceil_div_pos(lk, kFwdBN);
-    s.causal = p.causal ? (p.causal[b] != 0) : false;
+    s.H = ceil_div_pos(lk, kFwdBN);
+    s.causal = mask_is_causal(mt);
+    s.c = 2 + ceil_div(causal_offset(mt, lq, lk), kFwdBN);
     return s;
-  }
-  // first tile of the causal plateau W = y
-  static __device__ int plateau(const SeqSummary& s) { return max((s.y + 1) / 2 - 1, 0); }
-  static __device__ int items(const SeqSummary& s) { return s.x; }
-  static __device__ int work(const SeqSummary& s, int t) {
-    return s.causal ? min(s.y, 2 * t + 2) : s.y;
-  }
-  static __device__ int gt(const SeqSummary& s, int w) {
-    if (s.y <= w) return 0;
-    return s.causal ? max(s.x - w / 2, 0) : s.x;
-  }
-  static __device__ int eq(const SeqSummary& s, int w) {
-    if (!s.causal) return s.y == w ? s.x : 0;
-    if (w < s.y) return (w >= 2 && (w & 1) == 0 && w / 2 - 1 < s.x) ? 1 : 0;
-    return w == s.y ? s.x - min(s.x, plateau(s)) : 0;
-  }
-  static __device__ int before(const SeqSummary& s, int t, int w) {
-    if (!s.causal) return t;
-    return w == s.y ? t - min(t, plateau(s)) : 0;
   }
 };
 
@@ -180,7 +165,9 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
   const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, qrow_bytes));
   const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const bool causal = p.causal ? (p.causal[b] != 0) : false;
+  const int mtype = mask_type_of(p.causal, b);
+  const bool causal = mask_is_causal(mtype);
+  const int off = causal_offset(mtype, lq, lk);  // key j visible to query i iff j <= i + off
   const int hk = hq / p.group;
   const int q0 = tile_in_seq * BM;
   if (q0 >= lq) return;
@@ -188,8 +175,8 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   const int my_q = qw0 + r;
 
   int kv_end = lk;
-  if (causal && q0 + BM < kv_end) kv_end = q0 + BM;
-  const int n_kv_tiles = (kv_end + BN - 1) / BN;
+  if (causal && q0 + BM + off < kv_end) kv_end = q0 + BM + off;
+  const int n_kv_tiles = ceil_div_pos(kv_end, BN);  // 0: every row sees no key
 
   // Resources: this sequence's rows of head hq (q, o) and of head hk (k, v).
   const uint16_t* qbase = p.q + sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
@@ -285,7 +272,7 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
     const bool more = it + 1 < n_kv_tiles;
     if (more) load_tile(k0 + BN);
 
-    const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + kWaveM - 1);
+    const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + kWaveM - 1 + off);
     if (active) {
       const uint16_t* Kb = Ks + buf * KBUF;
       const uint16_t* Vb = Vt + buf * VBUF;
@@ -301,9 +288,10 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
         }
       }
 
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0);
+      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + off);
       if (need_mask) {
-        const int lim = causal ? (my_q + 1 < lk ? my_q + 1 : lk) : lk;  // keys j < lim visible
+        // keys j < lim visible (lim <= 0: none)
+        const int lim = causal ? (my_q + 1 + off < lk ? my_q + 1 + off : lk) : lk;
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt)
 #pragma unroll

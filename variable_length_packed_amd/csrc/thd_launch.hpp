@@ -13,7 +13,7 @@ struct Problem {
   const int32_t* cu_kv;
   const int32_t* pad_q;   // may be null
   const int32_t* pad_kv;  // may be null
-  const uint8_t* causal;  // may be null
+  const uint8_t* causal;  // per-sequence mask type (thd_mask_type); may be null
   int batch;
   int64_t T_q, T_kv;
   int h_q, h_kv, d;

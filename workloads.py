@@ -26,6 +26,11 @@ drawn in float32 and rounded to the storage dtype):
 * ``5``  -- cross attention, 32 pairs, q lengths uniform in [1, 512], kv
   lengths uniform in [1, 8192], full (no causal), bf16, h=16, d=128; the
   cu_seqlens buffers hold 2B+1 entries, the extra ones INT32_MAX; seed 5.
+* ``6``  -- bottom-right causal (the third mask type of the per-sequence
+  causal PR's maintainer review) on the chunked-prefill shape it serves:
+  32 sequences, a query chunk of U[64, 512] rows against a key/value history
+  of the chunk plus U[0, 4096] earlier rows, bf16, h=16, d=128, seed 6.
+  (The pages give no such workload; this one exercises the mask type.)
 """
 
 from dataclasses import dataclass, field
@@ -181,6 +186,12 @@ def config(name):
         lk = rng.integers(1, 8192, size=32, endpoint=True)
         return packed(lq, lk, causal=np.zeros(32, np.uint8), h_q=16, d=128,
                       dtype="bf16", extra_cu=32, seed=5, name="5")
+    if name == "6":
+        rng = np.random.default_rng(6)
+        lq = rng.integers(64, 512, size=32, endpoint=True)
+        lk = lq + rng.integers(0, 4096, size=32, endpoint=True)
+        return packed(lq, lk, causal=np.full(32, 2, np.uint8), h_q=16, d=128,
+                      dtype="bf16", seed=6, name="6")
     raise KeyError(name)
 
 
