@@ -262,9 +262,13 @@ def main():
         "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 4),
                            "min": round(step_ms[0], 4)},
         "config": {
-            "workload": (f"packed thd self-attention, config {w.name}: {w.batch} sequences, "
-                         f"{w.T_q} tokens, h_q={w.h_q} h_kv={w.h_kv} d={w.d} {w.dtype}, "
-                         f"{int(w.causal.sum())} causal, fwd+bwd incl. both padding masks"),
+            "workload": (f"packed thd {'self-' if w.self_attention else 'cross-'}attention, "
+                         f"config {w.name}: {w.batch} sequences, {w.T_q} query tokens"
+                         f"{'' if w.self_attention else f' / {w.T_kv} kv tokens'}, "
+                         f"h_q={w.h_q} h_kv={w.h_kv} d={w.d} {w.dtype}, "
+                         f"{int((w.causal == 1).sum())} top-left causal, "
+                         f"{int((w.causal == 2).sum())} bottom-right causal, "
+                         f"fwd+bwd incl. both padding masks"),
             "tokens": int(w.T_q), "batch": w.batch, "h_q": w.h_q, "h_kv": w.h_kv,
             "head_dim": w.d, "valid_pairs": int(pairs), "flops_per_step": int(flops),
             "seed": w.seed,
