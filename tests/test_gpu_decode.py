@@ -1,0 +1,74 @@
+"""GPU: the split-KV forward (few query rows per sequence against long key
+histories -- the KV-cache / decode shape) against the fp64 oracle.
+
+The forward takes this path whenever max_seqlen_q times the GQA group size is
+at most 32; the backward is the regular one.  Layouts vary the query rows
+per sequence (1-4), the key lengths (0 to a few thousand, so that sequences
+span several key splits), the GQA group, head dims, mask types (bottom-right
+causal is the decode mask) and pad rows."""
+import numpy as np
+import pytest
+import torch
+
+import variable_length_packed_amd as thd
+import workloads
+from gpu_helpers import dev_meta, gpu_fwd
+from test_gpu_attention import run_case
+
+pytestmark = pytest.mark.gpu
+
+
+def decode_layout(seed, batch, max_q, max_k, h_q, h_kv, d, dtype, types, slot_multiple=None,
+                  extra_cu=0, min_k=0):
+    rng = np.random.default_rng(seed)
+    lq = rng.integers(1, max_q, size=batch, endpoint=True)
+    lk = rng.integers(min_k, max_k, size=batch, endpoint=True)
+    mt = rng.choice(np.asarray(types, np.uint8), size=batch)
+    w = workloads.packed(lq, lk, causal=mt, h_q=h_q, h_kv=h_kv, d=d, dtype=dtype, seed=seed,
+                         slot_multiple=slot_multiple, extra_cu=extra_cu, name=f"dec{seed}")
+    assert w.max_seqlen_q * (h_q // h_kv) <= 32
+    return w
+
+
+CASES = [
+    dict(seed=201, batch=9, max_q=1, max_k=3000, h_q=8, h_kv=1, d=128, dtype="bf16", types=[2]),
+    dict(seed=202, batch=7, max_q=4, max_k=2500, h_q=16, h_kv=2, d=128, dtype="bf16",
+         types=[0, 1, 2]),
+    dict(seed=203, batch=6, max_q=2, max_k=1800, h_q=4, h_kv=4, d=64, dtype="fp16", types=[0, 2],
+         slot_multiple=16, extra_cu=3),
+    dict(seed=204, batch=8, max_q=3, max_k=700, h_q=2, h_kv=1, d=32, dtype="bf16", types=[1, 2],
+         min_k=0),
+    dict(seed=205, batch=5, max_q=4, max_k=5000, h_q=32, h_kv=8, d=96, dtype="fp16",
+         types=[2], min_k=2000),
+]
+
+
+@pytest.mark.parametrize("kw", CASES, ids=[f"d{c['seed']}" for c in CASES])
+def test_decode_layouts(kw):
+    run_case(decode_layout(**kw))
+
+
+def test_decode_rows_with_no_key():
+    # bottom-right causal with more query rows than keys, and empty histories:
+    # those rows are 0 with log-sum-exp -inf
+    w = workloads.packed([4, 3, 2, 4], [2, 0, 5, 1], causal=[2, 2, 0, 1], h_q=8, h_kv=2, d=64,
+                         dtype="bf16", seed=210, name="dec_nokey")
+    run_case(w)
+
+
+def test_decode_matches_the_tiled_forward():
+    # the same inputs through the tiled forward (max_seqlen_q raised above the
+    # split-KV bound) agree to the tolerance of the oracle comparison
+    w = decode_layout(seed=220, batch=6, max_q=4, max_k=2000, h_q=8, h_kv=1, d=128,
+                      dtype="bf16", types=[0, 1, 2])
+    q, k, v, _ = (t.cuda() for t in workloads.make_tensors(w))
+    m = dev_meta(w)
+    o1, l1 = gpu_fwd(w, q, k, v, m)
+    # max_seqlen_q is only a bound: 64 is above the split-KV limit
+    o2, l2 = thd.attn_fwd(q, k, v, m["cu_seqlens_q"], m["cu_seqlens_kv"], 64, w.max_seqlen_kv,
+                          is_causal=m["is_causal"], batch_size=m["batch_size"])
+    torch.cuda.synchronize()
+    assert (o1.float() - o2.float()).abs().max().item() < 2e-2
+    fin = torch.isfinite(l1)
+    assert torch.equal(fin, torch.isfinite(l2))
+    assert (l1[fin] - l2[fin]).abs().max().item() < 1e-3

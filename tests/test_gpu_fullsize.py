@@ -80,6 +80,6 @@ def check_config(name, n_row_seqs=3, n_full_seqs=2, max_full_len=1200):
     print(f"config {name}: ok", flush=True)
 
 
-@pytest.mark.parametrize("name", ["2", "3", "5", "4", "6"])
+@pytest.mark.parametrize("name", ["2", "3", "5", "4", "6", "7"])
 def test_full_size_config(name):
     check_config(name)

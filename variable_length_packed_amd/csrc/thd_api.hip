@@ -38,6 +38,8 @@ int to_problem(const thd_varlen_args* a, thd::Problem* p) {
   p->pad_kv = a->cu_seqlens_kv_padded;
   p->causal = a->mask_type;
   p->batch = a->batch;
+  p->max_q = a->max_seqlen_q;
+  p->max_kv = a->max_seqlen_kv;
   p->T_q = a->total_q;
   p->T_kv = a->total_kv;
   p->h_q = a->h_q;

@@ -384,13 +384,38 @@ int64_t fwd_tile_bound(const Problem& p) { return (p.T_q + kFwdBM - 1) / kFwdBM 
 
 }  // namespace
 
-// The attention workgroups' schedule: 2 + 2 * query-tile bound int32.
+// The attention workgroups' schedule: 2 + 2 * query-tile bound int32; or,
+// for few query rows per sequence, the split-KV partials.
 size_t fwd_workspace_bytes(const Problem& p) {
+  if (decode_applies(p)) return decode_workspace_bytes(p);
   return p.batch > 0 ? (size_t)(2 + 2 * fwd_tile_bound(p)) * sizeof(int32_t) : 0;
+}
+
+static FwdParams pad_params(const Problem& p, void* o, float* lse) {
+  FwdParams fp = {};
+  fp.o = (uint16_t*)o;
+  fp.lse = lse;
+  fp.cu_q = p.cu_q;
+  fp.pad_q = p.pad_q;
+  fp.T_q = p.T_q;
+  fp.batch = p.batch;
+  fp.h_q = p.h_q;
+  fp.d = p.d;
+  fp.n_sched = 0;
+  return fp;
+}
+
+hipError_t launch_fwd_pad_rows(const Problem& p, void* o, float* lse, hipStream_t s) {
+  const int64_t n_zero = (p.T_q + kZeroRows - 1) / kZeroRows;
+  if (n_zero == 0) return hipSuccess;
+  hipLaunchKernelGGL(thd_fwd_pre_kernel, dim3((unsigned)n_zero), dim3(256), 0, s,
+                     pad_params(p, o, lse));
+  return hipGetLastError();
 }
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, void* workspace, hipStream_t s) {
+  if (decode_applies(p)) return launch_decode(p, q, k, v, o, lse, workspace, s);
   FwdParams fp;
   fp.q = (const uint16_t*)q;
   fp.k = (const uint16_t*)k;

@@ -15,6 +15,7 @@ struct Problem {
   const int32_t* pad_kv;  // may be null
   const uint8_t* causal;  // per-sequence mask type (thd_mask_type); may be null
   int batch;
+  int max_q, max_kv;      // host bounds on the sequence lengths
   int64_t T_q, T_kv;
   int h_q, h_kv, d;
   float scale;
@@ -25,6 +26,15 @@ hipError_t launch_padding_mask(const int32_t* cu, int batch, int max_seqlen, uin
                                hipStream_t s);
 
 size_t fwd_workspace_bytes(const Problem& p);
+
+// Zeros on the pad rows of o and -inf on their LSE (the forward's pad pass).
+hipError_t launch_fwd_pad_rows(const Problem& p, void* o, float* lse, hipStream_t s);
+
+// Split-KV forward for few query rows per sequence (see thd_decode.hip).
+bool decode_applies(const Problem& p);
+size_t decode_workspace_bytes(const Problem& p);
+hipError_t launch_decode(const Problem& p, const void* q, const void* k, const void* v, void* o,
+                         float* lse, void* workspace, hipStream_t s);
 
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, void* workspace, hipStream_t s);

@@ -31,6 +31,10 @@ drawn in float32 and rounded to the storage dtype):
   32 sequences, a query chunk of U[64, 512] rows against a key/value history
   of the chunk plus U[0, 4096] earlier rows, bf16, h=16, d=128, seed 6.
   (The pages give no such workload; this one exercises the mask type.)
+* ``7``  -- the KV-cache / decode shape: 64 sequences of U[1, 4] new query
+  tokens against U[256, 16384] keys (history included), bottom-right causal,
+  GQA 32 query / 8 kv heads, bf16, d=128, seed 7.  Also not on the pages;
+  it exercises the split-KV forward.
 """
 
 from dataclasses import dataclass, field
@@ -192,6 +196,12 @@ def config(name):
         lk = lq + rng.integers(0, 4096, size=32, endpoint=True)
         return packed(lq, lk, causal=np.full(32, 2, np.uint8), h_q=16, d=128,
                       dtype="bf16", seed=6, name="6")
+    if name == "7":
+        rng = np.random.default_rng(7)
+        lq = rng.integers(1, 4, size=64, endpoint=True)
+        lk = rng.integers(256, 16384, size=64, endpoint=True)
+        return packed(lq, lk, causal=np.full(64, 2, np.uint8), h_q=32, h_kv=8, d=128,
+                      dtype="bf16", seed=7, name="7")
     raise KeyError(name)
 
 
