@@ -40,6 +40,9 @@ def parse():
     ap.add_argument("--spinup-seconds", type=float, default=1.5)
     ap.add_argument("--config", default="2")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fwd-only", action="store_true",
+                    help="time the padding masks and the forward only, against the HBM "
+                         "roofline (for the split-KV decode workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (read + write) a few "
@@ -190,6 +193,8 @@ def main():
         _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
                                     fws_bytes, stream), "fwd")
         evs[1].record(cur)
+        if a.fwd_only:
+            return
         _lib.check(lib.thd_attn_bwd_timed(args, P["q"], P["k"], P["v"], P["o"], P["do"],
                                           P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
                                           ws_bytes, stream, ev_arrays[i]), "bwd")
@@ -201,6 +206,8 @@ def main():
                    "mask kv")
         _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
                                     fws_bytes, stream), "fwd")
+        if a.fwd_only:
+            return
         _lib.check(lib.thd_attn_bwd(args, P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"],
                                     P["dq"], P["dk"], P["dv"], P["ws"], ws_bytes, stream), "bwd")
 
@@ -219,6 +226,9 @@ def main():
     elapsed = time.perf_counter() - t0
 
     timed = events[a.warmup:]
+    if a.fwd_only:
+        print(json.dumps(fwd_only_result(a, w, timed, elapsed)), flush=True)
+        return
     fwd_ms = [e[0].elapsed_time(e[1]) for e in timed]
     pre_ms = [e[2].elapsed_time(e[3]) for e in timed]
     main_ms = [e[3].elapsed_time(e[4]) for e in timed]
@@ -282,6 +292,52 @@ def main():
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, q, k, v, do, a.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def fwd_only_result(a, w, timed, elapsed):
+    """The forward alone (with both padding masks), against the HBM roofline:
+    algorithmic bytes = valid q, k, v read once (k, v at h_kv) + o written over
+    all query rows + the log-sum-exp."""
+    from variable_length_packed_amd.metrics import attention_flops, valid_pairs
+    import numpy as np
+    mean = lambda xs: sum(xs) / len(xs)
+    fwd_ms = [e[0].elapsed_time(e[1]) for e in timed]
+    mask_ms = [e[6].elapsed_time(e[0]) for e in timed]
+    step_ms = sorted(e[6].elapsed_time(e[1]) for e in timed)
+    pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, w.h_q)
+    flops = attention_flops(pairs, w.d, "fwd")
+    elem = 2
+    nbytes = (int(np.sum(w.lens_q)) * w.h_q * w.d * elem
+              + 2 * int(np.sum(w.lens_kv)) * w.h_kv * w.d * elem
+              + int(w.T_q) * w.h_q * w.d * elem + int(w.T_q) * w.h_q * 4)
+    f_ms = mean(fwd_ms)
+    gbs = nbytes / (f_ms * 1e-3) / 1e9
+    value = flops / (elapsed / a.steps) / 1e12
+    return {
+        "metric": "packed-THD attention valid-pair TFLOP/s fwd only",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(elapsed * 1e3 / a.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "fp16", "data": "synthetic",
+        "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 4),
+                           "min": round(step_ms[0], 4)},
+        "config": {
+            "workload": (f"packed thd attention, config {w.name}: {w.batch} sequences, "
+                         f"{w.T_q} query tokens / {w.T_kv} kv tokens, h_q={w.h_q} "
+                         f"h_kv={w.h_kv} d={w.d} {w.dtype}, {int((w.causal == 2).sum())} "
+                         f"bottom-right causal, forward incl. both padding masks"),
+            "tokens": int(w.T_q), "batch": w.batch, "valid_pairs": int(pairs),
+            "flops_per_step": int(flops), "algorithmic_bytes": int(nbytes), "seed": w.seed,
+        },
+        "kernel_ms": {"masks": round(mean(mask_ms), 4), "fwd": round(f_ms, 4)},
+        "roofline": {"bound": "hbm", "kernel": "thd_attn_fwd (all its launches)",
+                     "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None,
+                     "avg_launch_ms": round(f_ms, 4)},
+        "cpu_baseline": None,
+    }
 
 
 if __name__ == "__main__":

@@ -158,8 +158,12 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, 
     return out, lse
 
 
-def fwd_workspace_size(q, k, cu_seqlens_q, cu_seqlens_kv, batch_size=None):
-    a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, 0, 0, None, None, None, None, batch_size)
+def fwd_workspace_size(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
+                       batch_size=None):
+    """Bytes of workspace ``attn_fwd`` needs (the split-KV path for few query
+    rows per sequence sizes it from the max_seqlen bounds)."""
+    a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, None, None,
+                   None, None, batch_size)
     return int(_lib.load().thd_attn_fwd_workspace_size(a))
 
 
