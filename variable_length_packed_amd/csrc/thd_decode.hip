@@ -286,7 +286,7 @@ DecodeShape decode_shape(const Problem& p) {
   // chunks of at least two steps
   int ck = 2048;
   const int64_t units = (int64_t)p.batch * p.h_kv;
-  while (ck > 2 * kDecStep && units * ((p.max_kv + ck - 1) / ck) < 4096) ck /= 2;
+  while (ck > 2 * kDecStep && units * ((p.max_kv + ck - 1) / ck) < 16384) ck /= 2;
   DecodeShape ds;
   ds.ck = ck;
   ds.n_split = p.max_kv > 0 ? (p.max_kv + ck - 1) / ck : 1;
