@@ -1,12 +1,13 @@
 // Forward attention over packed variable-length ("thd") tensors.
 //
 // Computes, per sequence and query head, softmax(scale * Q K^T + mask) V with
-// the per-sequence causal flag of TransformerEngine PR "Add per-sequence
-// causal policy to packed THD attention" (Description; top-left causal), the
-// padded slot starts of that PR's two-call example (maintainer review), and
-// pad rows written as zeros.  The mask of sequence b is derived inline from
-// cu_seqlens (key j visible iff j < lk_b, and j <= i when causal), so no mask
-// tensor is read and the host never synchronises.
+// the per-sequence causal policy of TransformerEngine PR "Add per-sequence
+// causal policy to packed THD attention" (Description; the mask types of its
+// maintainer review: padding, top-left and bottom-right causal), the padded
+// slot starts of that PR's two-call example, and pad rows written as zeros.
+// The mask of sequence b is derived inline from cu_seqlens (key j visible iff
+// j < lk_b and, when causal, j <= i + off with off = 0 or lk_b - lq_b), so no
+// mask tensor is read and the host never synchronises.
 //
 // One workgroup = 4 waves = one (sequence, 128-row query tile, query head)
 // work item.  A pre pass ranks the (sequence, query tile) items by the number
@@ -266,6 +267,11 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
     store_tile(0);
   }
   __syncthreads();
+  // Nothing is in flight here (store_tile waited for its loads).  Saying so
+  // keeps the compiler from treating the Q operand loads as pending at the
+  // loop head, where it would otherwise wait, inside the S products, for the
+  // next tile's prefetch as well.
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   for (int it = 0; it < n_kv_tiles; ++it) {
     const int k0 = it * BN;
     const int buf = it & 1;
