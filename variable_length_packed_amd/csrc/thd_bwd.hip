@@ -164,28 +164,15 @@ __device__ __forceinline__ uint32_t swz_ds(int row, int kv) {
 // a handful of bases live instead of one register per address.
 //   S / dP operands:   swz(r, 16c + 8h)         = swz(r, 8h) ^ (c << 5)
 //                      (same for key row 32w + r, since f(32w + r) = f(r))
-//   dV / dK operands:  swz(R + 16kb + 8j, C + 32dt), R = 4h + tr_row < 8
-//                        = swz(R, C) ^ ((16kb + 8j) * 2DP) ^ ((4dt ^ 8j') << 4)
-//                      with j' = j when DP = 128 (f's bit 3 follows row bit 3)
+//   dV / dK operands:  swz(R + 16kb + 8j, C + 32dt) = swz(R, C) ^ tr_xor(dt, kb, j)
 //   dS writes:         swz_ds(8m + 4h + e, kv)  = swz_ds(4h, kv) ^ ((8m + e) << 9)
 //                                                 ^ ((8(m & 1) + e) << 4)
 //   dQ, dS reads:      swz_ds(16qh + g, 32st + 8grp) = swz_ds(g, 8grp) ^ (qh << 13)
 //                                                      ^ (st << 6)
 //   dQ, K^T reads:     swz(32st + R' + 4j, C), R' = 8grp + tr_row
 //                        = swz(R', C) ^ ((32st + 4j) * 2DP) ^ (j << 4)
-template <int DP>
-__device__ __forceinline__ uint32_t tr_xor(int dt, int kb, int j) {
-  return (uint32_t)((16 * kb + 8 * j) * DP * 2) ^ ((uint32_t)(4 * dt ^ (DP == 128 ? 8 * j : 0)) << 4);
-}
 __device__ __forceinline__ uint32_t ds_xor(int m, int e) {
   return ((uint32_t)(8 * m + e) << 9) ^ ((uint32_t)(8 * (m & 1) + e) << 4);
-}
-
-// Makes v opaque to the optimiser: values derived from it are formed where
-// they are used instead of being hoisted out of the loop into registers.
-__device__ __forceinline__ uint32_t opaque(uint32_t v) {
-  asm volatile("" : "+v"(v));
-  return v;
 }
 
 template <class DT, int DP>

@@ -105,6 +105,37 @@ __device__ __forceinline__ u32x4 buf_load16(rsrc_t r, uint32_t voff, uint32_t so
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
 }
 
+// The four descriptor words make_rsrc builds (stride 0), made wave-uniform,
+// for use as an assembly operand.
+__device__ __forceinline__ u32x4 rsrc_words(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)(uintptr_t)base;
+  u32x4 w;
+  w[0] = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  w[1] = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32) & 0xffffu);
+  w[2] = __builtin_amdgcn_readfirstlane(bytes);
+  w[3] = (uint32_t)kRsrcWord3;
+  return w;
+}
+
+// LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from a buffer straight into LDS: lane i of the wave
+// writes LDS byte lds_wave + 16 i (lds_wave is made wave-uniform; it goes to
+// M0); a lane whose offset is out of range writes zeros.  The wave's vmcnt
+// counts the load until its data is in LDS: the caller waits for it and
+// synchronises the workgroup before the tile is read.  Written as assembly:
+// the compiler cannot tell the tile being filled from the tiles being read
+// and would otherwise wait for the load before every transpose read of LDS.
+__device__ __forceinline__ void buf_load_lds16(u32x4 rs, uint32_t lds_wave, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds_wave)), "v"(voff), "s"(rs)
+               : "m0", "memory");
+}
+
 __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, 0);
 }
@@ -145,6 +176,35 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* lds, uint32_t 
   typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
   const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(lds + byte_off));
   return __builtin_bit_cast(u32x2, v);
+}
+
+// Transpose-read operand of a 32x32x16 product whose contraction runs over
+// tile rows: A lane (r, h) takes column C + 32dt (C = 16(grp & 1) + 4(g16 & 3),
+// read through the transpose) of rows 16kb + 4h + {0..3} (j = 0) and
+// 16kb + 8 + 4h + {0..3} (j = 1).  With R = 4h + (g16 >> 2) < 8,
+//   swz(R + 16kb + 8j, C + 32dt) = swz(R, C) ^ tr_xor(dt, kb, j):
+// the row offset is a multiple of 8 added to R < 8, f sees only its bit 3
+// (as chunk bit 3, kept when DP = 128), and 4dt lies above C's chunk bits.
+// The row part only sets row bits that are zero in swz(R, C), so it may also
+// be added (and then ride in an instruction's offset field).
+template <int DP>
+__device__ __forceinline__ uint32_t tr_row(int kb, int j) {
+  return (uint32_t)((16 * kb + 8 * j) * DP * 2);
+}
+template <int DP>
+__device__ __forceinline__ uint32_t tr_chunk(int dt, int j) {
+  return (uint32_t)(4 * dt ^ (DP == 128 ? 8 * j : 0)) << 4;
+}
+template <int DP>
+__device__ __forceinline__ uint32_t tr_xor(int dt, int kb, int j) {
+  return tr_row<DP>(kb, j) ^ tr_chunk<DP>(dt, j);
+}
+
+// Makes v opaque to the optimiser: values derived from it are formed where
+// they are used instead of being hoisted out of the loop into registers.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
 }
 
 __device__ __forceinline__ u32x4 cat2(u32x2 a, u32x2 b) {

@@ -16,9 +16,10 @@
 // query rows.  Scores are computed transposed, S^T = K Q^T, so that a lane
 // owns one query row: the row max needs one exchange between wave halves and
 // the probabilities land directly in the B-operand layout of O^T = V^T P^T.
-// K tiles are staged in LDS row-major, V tiles transposed (with the K-slot
-// permutation that matches the accumulator layout of S^T).  The pre pass also
-// writes zeros to pad rows of O and -inf to their LSE.
+// K and V tiles go from memory straight into LDS (no register staging),
+// row-major with swizzled 16-byte chunks, double buffered; the V^T operand of
+// the PV product comes from transpose reads.  The pre pass also writes zeros
+// to pad rows of O and -inf to their LSE.
 #include "thd_common.hpp"
 #include "thd_launch.hpp"
 
@@ -78,14 +79,6 @@ struct FwdSchedModel {
   }
 };
 
-// Position of key group g4 (4 keys) inside a 16-key block of the transposed
-// V tile: groups 1 and 2 trade places, so that lane half h reads keys
-// {4h..4h+3, 8+4h..8+4h+3} of the block as 8 contiguous elements, which is
-// the order in which the S^T accumulator holds them.
-__device__ __forceinline__ int vt_group_pos(int g4) {
-  return (g4 == 1) ? 2 : (g4 == 2) ? 1 : g4;
-}
-
 // Zero the pad rows [r0, r0 + kZeroRows) of O and set their LSE to -inf.
 __device__ void fwd_zero_pad_rows(const FwdParams& p, int zb) {
   __shared__ uint8_t invalid[kZeroRows];
@@ -132,16 +125,14 @@ constexpr float kRescaleLog2 = 8.0f;
 template <class DT, int DP>
 __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBM, BN = kFwdBN;
-  constexpr int KST = DP + 8;      // LDS row stride of K (elements)
-  constexpr int VST = BN + 8;      // LDS row stride of V^T (elements)
   constexpr int NC = DP / 16;      // 16-wide d blocks (MFMA K steps of S^T)
   constexpr int ND = DP / 32;      // 32-row d tiles of O^T
   constexpr int KCH = DP / 8;      // 16-byte chunks per K row
-  constexpr int KLOADS = BN * KCH / 256;
-  constexpr int VTHREADS = 2 * DP; // 16 key groups x DP/8 chunks
-  constexpr int KBUF = BN * KST, VBUF = DP * VST;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * KBUF];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[2 * VBUF];
+  constexpr int TILE = BN * DP * 2;  // bytes of one K or V tile
+  constexpr int BPW = TILE / 1024 / 4;  // 1 KB blocks (one load each) per wave per tile
+  static_assert(BPW >= 1 && BPW * 4096 == TILE, "tile splits into 1 KB blocks over 4 waves");
+  // buffer j: K tile at 2j * TILE, V tile at (2j + 1) * TILE
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
 
   // Workgroups in schedule order (largest items first), query heads minor:
   // with h_q a multiple of 8, head hq always lands on XCD hq % 8, whose L2
@@ -155,10 +146,12 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = uniform(tid >> 6);
   const int l = tid & 63;
   const int r = l & 31;
   const int h = l >> 5;
+  const int g16 = l & 15;
+  const int grp = l >> 4;
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
@@ -202,86 +195,60 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   float m_run = -__builtin_inff();  // running max of the raw scores (stale up to 2^8)
   float l_run = 0.f;                // this lane's share of the row sum
 
-  // Per-thread offsets of the K / V chunks it stages (relative to a tile).
-  uint32_t koff[KLOADS];
+  // Tile staging: load n of wave w fills 1 KB block BPW * w + n of a tile,
+  // lane l the 16-byte slot 64 * block + l, i.e. row slot / KCH, swizzled
+  // chunk x = slot % KCH, which holds memory chunk x ^ f(row).  The same
+  // offsets (relative to the tile's first row) serve K and V; chunks past d
+  // and rows past lk read as zeros.
+  uint32_t loff[BPW];
 #pragma unroll
-  for (int i = 0; i < KLOADS; ++i) {
-    const int cid = tid + 256 * i;
-    const int row = cid / KCH;
-    const int c = cid - row * KCH;
-    koff[i] = 8 * c < p.d ? (uint32_t)row * kvrow_bytes + 16u * c : kOobOffset;
+  for (int n = 0; n < BPW; ++n) {
+    const int slot = 64 * (BPW * w + n) + l;
+    const int row = slot / KCH;
+    const int x = slot - row * KCH;
+    const int gc = x ^ (int)((swz<DP>(row, 0) >> 4) & (KCH - 1));
+    loff[n] = 8 * gc < p.d ? (uint32_t)row * kvrow_bytes + 16u * gc : kOobOffset;
   }
-  const int v_grp = tid & 15;    // key group of 4 keys
-  const int v_chunk = tid >> 4;  // 8-wide d chunk
-  const uint32_t voff0 = 8 * v_chunk < p.d && tid < VTHREADS
-                             ? (uint32_t)(4 * v_grp) * kvrow_bytes + 16u * v_chunk
-                             : kOobOffset;
-
-  u32x4 kreg[KLOADS];
-  u32x4 vreg[4];
-  auto load_tile = [&](int k0) {
+  auto load_tile = [&](int k0, int buf) {
     const uint32_t left = (uint32_t)(lk - k0);  // >= 1 for every tile we visit
-    const rsrc_t k_rs = make_rsrc(kbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
-    const rsrc_t v_rs = make_rsrc(vbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const u32x4 k_rs = rsrc_words(kbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const u32x4 v_rs = rsrc_words(vbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const uint32_t kt = lds_addr(smem) + (uint32_t)(2 * buf * TILE + 1024 * BPW * w);
 #pragma unroll
-    for (int i = 0; i < KLOADS; ++i) kreg[i] = buf_load16(k_rs, koff[i], 0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      vreg[i] = buf_load16(v_rs, voff0 == kOobOffset ? kOobOffset : voff0 + i * kvrow_bytes, 0);
-  };
-
-  auto store_tile = [&](int buf) {
-    uint16_t* Kb = Ks + buf * KBUF;
-    uint16_t* Vb = Vt + buf * VBUF;
-#pragma unroll
-    for (int i = 0; i < KLOADS; ++i) {
-      const int cid = tid + 256 * i;
-      const int row = cid / KCH;
-      const int c = cid - row * KCH;
-      *(u32x4*)(&Kb[row * KST + 8 * c]) = kreg[i];
-    }
-    if (tid < VTHREADS) {
-      // 4 keys x 8 d  ->  8 rows of V^T with 4 keys each
-      const int pos = 16 * (v_grp >> 2) + 4 * vt_group_pos(v_grp & 3);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int word = e >> 1;
-        const uint32_t x0 = vreg[0][word], x1 = vreg[1][word], x2 = vreg[2][word],
-                       x3 = vreg[3][word];
-        u32x2 out;
-        if (!(e & 1)) {
-          out[0] = __builtin_amdgcn_perm(x1, x0, 0x05040100u);
-          out[1] = __builtin_amdgcn_perm(x3, x2, 0x05040100u);
-        } else {
-          out[0] = __builtin_amdgcn_perm(x1, x0, 0x07060302u);
-          out[1] = __builtin_amdgcn_perm(x3, x2, 0x07060302u);
-        }
-        *(u32x2*)(&Vb[(8 * v_chunk + e) * VST + pos]) = out;
-      }
+    for (int n = 0; n < BPW; ++n) {
+      buf_load_lds16(k_rs, kt + 1024 * n, loff[n]);
+      buf_load_lds16(v_rs, kt + TILE + 1024 * n, loff[n]);
     }
   };
+  // Operand addresses inside a tile (see swz and tr_xor); row parts set bits
+  // that are zero in the base and are added, so they ride in the offset
+  // field, as do the buffer's K / V choice:
+  //   K rows 32tt + r, chunk 2c + h:  (b_k ^ (c << 5)) + 32tt * 2DP
+  //   V^T operand (dt, kb, j):        (b_t ^ tr_chunk(dt, j)) + tr_row(kb, j)
+  const uint32_t b_k = swz<DP>(r, 8 * h);
+  const uint32_t b_t = swz<DP>(4 * h + (g16 >> 2), 16 * (grp & 1) + 4 * (g16 & 3));
 
   const float c2 = p.c2;
-  if (n_kv_tiles > 0) {
-    load_tile(0);
-    store_tile(0);
-  }
+  if (n_kv_tiles > 0) load_tile(0, 0);
+  // vmcnt(0): the first tile and the Q operand are in.  Saying so also keeps
+  // the compiler from treating the Q loads as pending at the loop head, where
+  // it would otherwise wait, inside the S products, for the next tile.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
-  // Nothing is in flight here (store_tile waited for its loads).  Saying so
-  // keeps the compiler from treating the Q operand loads as pending at the
-  // loop head, where it would otherwise wait, inside the S products, for the
-  // next tile's prefetch as well.
-  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
   for (int it = 0; it < n_kv_tiles; ++it) {
     const int k0 = it * BN;
     const int buf = it & 1;
     const bool more = it + 1 < n_kv_tiles;
-    if (more) load_tile(k0 + BN);
+    // The other buffer was last read in the previous iteration, which every
+    // wave has left (barrier below).
+    if (more) load_tile(k0 + BN, buf ^ 1);
 
     const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + kWaveM - 1 + off);
     if (active) {
-      const uint16_t* Kb = Ks + buf * KBUF;
-      const uint16_t* Vb = Vt + buf * VBUF;
+      // per-iteration bases (kept opaque so that the XORs are formed here and
+      // not hoisted into one register per address)
+      const uint32_t bo = (uint32_t)(2 * buf * TILE);
+      const uint32_t a_k = opaque(b_k + bo), a_t = opaque(b_t + bo);
       // S^T tiles: rows = keys k0 + 32*tt + (C row), columns = this wave's queries
       f32x16 s[2];
 #pragma unroll
@@ -289,7 +256,7 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
         s[tt] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
-          const u32x4 a = *(const u32x4*)(&Kb[(32 * tt + r) * KST + 16 * c + 8 * h]);
+          const u32x4 a = *(const u32x4*)(smem + ((a_k ^ (uint32_t)(c << 5)) + 32 * tt * DP * 2));
           s[tt] = DT::mfma(as_vec8<DT>(a), qreg[c], s[tt]);
         }
       }
@@ -348,11 +315,13 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const u32x4 a = *(const u32x4*)(&Vb[(32 * dt + r) * VST + 16 * kb + 8 * h]);
+          const u32x4 a =
+              cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + TILE + tr_row<DP>(kb, 0)),
+                   lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + TILE + tr_row<DP>(kb, 1)));
           acc[dt] = DT::mfma(as_vec8<DT>(a), pb[kb], acc[dt]);
         }
     }
-    if (more) store_tile(buf ^ 1);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of the next tile is in LDS
     __syncthreads();
   }
 
