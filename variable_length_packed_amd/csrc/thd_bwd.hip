@@ -44,7 +44,7 @@ struct BwdParams {
   uint16_t* dq;
   uint16_t* dk;
   uint16_t* dv;
-  float* dq_acc;  // [T_q, h_q, d]
+  float* dq_acc;  // [T_q, h_q, DP], row-major like dq
   float* dsum;    // [h_q, T_q], holds -D
   float* lsum;    // [h_q, T_q], holds -LSE / scale
   int32_t* sched; // [2 + 2 * n_kv_tiles]: item count, then (sequence, key tile) by rank
@@ -62,7 +62,8 @@ struct BwdParams {
 };
 
 // ---------------------------------------------------------------------------
-// pre: -D = -rowsum(dO * O) in fp32, and dq_acc = 0.  16 lanes per (row, head).
+// pre: -D = -rowsum(dO * O) in fp32, -LSE / scale, and dq_acc = 0; DP / 8 lanes
+// per (row, head).
 // ---------------------------------------------------------------------------
 // Schedule of the main kernel (largest first, see build_schedule): key tile
 // kt of sequence b walks W = ceil(lq / BQ) query tiles, or, with a causal
@@ -74,11 +75,12 @@ static_assert(kBwdBK == 8 * kBwdBQ, "work model assumes eight query tiles per ke
 struct BwdSchedModel {
   static constexpr int kSlope = -8;
   const BwdParams& p;
+  int64_t acc_row_bytes;  // accumulator row: the main kernel's clamp of lq
   __device__ SeqSummary seq(int b) const {
     const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
     const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
     const int lq =
-        clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, (int64_t)p.h_q * p.d * 4);
+        clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, acc_row_bytes);
     const int lk =
         clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
     const int mt = mask_type_of(p.causal, b);
@@ -91,47 +93,64 @@ struct BwdSchedModel {
   }
 };
 
+// (row, head) pairs per pre / post workgroup: KCH = DP / 8 lanes per pair
+// (one 16-byte chunk each), 256 / KCH lane groups, two pairs per group.
+template <int DP>
+constexpr int kPairsPerBlock = 2 * 256 / (DP / 8);
+
 template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   if ((int)blockIdx.x < p.n_sched) {
-    build_schedule(BwdSchedModel{p}, p.batch, p.n_kv_tiles, p.sched,
+    build_schedule(BwdSchedModel{p, (int64_t)p.h_q * DP * 4}, p.batch, p.n_kv_tiles, p.sched,
                    blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
-  const int64_t pair = (int64_t)(blockIdx.x - p.n_sched) * 16 + (threadIdx.x >> 4);
-  const int c = threadIdx.x & 15;
-  if (pair >= p.T_q * p.h_q) return;  // whole 16-lane groups leave together
-  const int64_t row = pair / p.h_q;
-  const int hh = (int)(pair - row * p.h_q);
+  // Pairs in row-major order (pair = row * h_q + head), so that o, dout and
+  // the accumulator rows cleared are each one stream.
+  constexpr int KCH = DP / 8, PB = kPairsPerBlock<DP>;
+  const int64_t pairs = p.T_q * p.h_q;
+  const int64_t p0 = (int64_t)((int)blockIdx.x - p.n_sched) * PB;
+  const int g = threadIdx.x / KCH;
+  const int c = threadIdx.x % KCH;
   // Every row is processed, pad rows included: the main kernel reads -D and
   // -LSE/scale only at rows inside a sequence (through range-limited
   // resources), and the accumulator of a pad row receives no atomics, so it
   // stays zero and converts to the +0 the pad rows of dq need.
-  const int64_t off = row * (int64_t)p.h_q * p.d + (int64_t)hh * p.d + 8 * c;
-  float acc = 0.f;
-  if (8 * c < p.d) {
-    const u32x4 a = *(const u32x4*)(p.o + off);
-    const u32x4 g = *(const u32x4*)(p.dout + off);
+  int64_t pr[2];
+  u32x4 a[2], gr[2];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      acc += DT::to_f32((uint16_t)(a[w] & 0xffffu)) * DT::to_f32((uint16_t)(g[w] & 0xffffu));
-      acc += DT::to_f32((uint16_t)(a[w] >> 16)) * DT::to_f32((uint16_t)(g[w] >> 16));
+  for (int t = 0; t < 2; ++t) {
+    pr[t] = p0 + g + t * (PB / 2);
+    a[t] = gr[t] = u32x4{0u, 0u, 0u, 0u};
+    if (pr[t] < pairs && 8 * c < p.d) {
+      const int64_t off = pr[t] * p.d + 8 * c;  // o, dout: [T_q][h_q][d]
+      a[t] = *(const u32x4*)(p.o + off);
+      gr[t] = *(const u32x4*)(p.dout + off);
     }
   }
-  if (8 * c < DP) {
-    // accumulator layout [h_q][T_q][DP]
-    float* dst = p.dq_acc + ((int64_t)hh * p.T_q + row) * DP + 8 * c;
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    *(f32x4*)dst = z;
-    *(f32x4*)(dst + 4) = z;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    if (pr[t] < pairs) {
+      float* dst = p.dq_acc + pr[t] * DP + 8 * c;
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      *(f32x4*)dst = z;
+      *(f32x4*)(dst + 4) = z;
+    }
+    float acc = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      acc += DT::to_f32((uint16_t)(a[t][w] & 0xffffu)) * DT::to_f32((uint16_t)(gr[t][w] & 0xffffu));
+      acc += DT::to_f32((uint16_t)(a[t][w] >> 16)) * DT::to_f32((uint16_t)(gr[t][w] >> 16));
+    }
+#pragma unroll
+    for (int m = KCH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, KCH);
+    if (pr[t] < pairs && c < 2) {
+      const int64_t row = pr[t] / p.h_q;
+      const int64_t i = (pr[t] - row * p.h_q) * p.T_q + row;  // statistics: [h_q][T_q]
+      if (c == 0) p.dsum[i] = -acc;                           // -D
+      else p.lsum[i] = p.lse[i] * (-1.0f / p.scale);          // -LSE / scale
+    }
   }
-  acc += __shfl_xor(acc, 8, 16);
-  acc += __shfl_xor(acc, 4, 16);
-  acc += __shfl_xor(acc, 2, 16);
-  acc += __shfl_xor(acc, 1, 16);
-  const int64_t i = (int64_t)hh * p.T_q + row;
-  if (c == 0) p.dsum[i] = -acc;                         // -D
-  if (c == 1) p.lsum[i] = p.lse[i] * (-1.0f / p.scale);  // -LSE / scale
 }
 
 // ---------------------------------------------------------------------------
@@ -216,7 +235,7 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const uint32_t accrow_bytes = (uint32_t)p.h_q * p.d * 4;
+  const uint32_t accrow_bytes = (uint32_t)p.h_q * DP * 4;
   const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
   const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
   const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
@@ -315,19 +334,23 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
   int hq_p = hq, q0_p = q0;  // query tile that dq belongs to
   const int dcol = 16 * w + g16;
-  // Atomic j (0..7) adds dq[j / 4][j % 4]: rows past lq fall outside the
-  // resource and are dropped; accumulator layout [h_q][T_q][DP]: the 4 rows
-  // of a lane are immediate offsets.
+  // Atomic j (0..7) adds dq[j / 4][j % 4] to row q0 + 4grp + 16(j / 4) + j % 4
+  // of the accumulator ([T_q][h_q][DP]; the resource starts at this head's
+  // first row of the sequence, rows accrow_bytes apart): rows past lq fall
+  // outside the resource and are dropped.
   rsrc_t acc_rs;
   uint32_t acc_base = kOobOffset;
   auto setup_dq = [&](bool real) {
-    acc_rs = make_rsrc(p.dq_acc + ((int64_t)hq_p * p.T_q + sq) * DP, (uint32_t)lq * (DP * 4));
-    acc_base = (real && dcol < p.d) ? (uint32_t)((q0_p + 4 * grp) * DP + dcol) * 4u : kOobOffset;
+    acc_rs = make_rsrc(p.dq_acc + (sq * p.h_q + hq_p) * DP, (uint32_t)lq * accrow_bytes);
+    acc_base = (real && dcol < p.d) ? (uint32_t)(q0_p + 4 * grp) * accrow_bytes + dcol * 4u
+                                    : kOobOffset;
   };
   auto atomic_dq = [&](int j) {
     const int qh = j >> 2, e = j & 3;
     buf_atomic_add(dq[qh][e], acc_rs,
-                   acc_base == kOobOffset ? kOobOffset : acc_base + (16 * qh + e) * DP * 4, 0);
+                   acc_base == kOobOffset ? kOobOffset
+                                          : acc_base + (uint32_t)(16 * qh + e) * accrow_bytes,
+                   0);
   };
   auto flush_dq = [&](bool real) {
     setup_dq(real);
@@ -565,28 +588,42 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
 // post: dq = scale * dq_acc in the storage dtype; zero pad rows of dk / dv.
 // ---------------------------------------------------------------------------
 template <class DT, int DP>
-__global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int64_t n_chunks,
-                                                           int n_conv_wg) {
+__global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int n_conv_wg) {
   const int tid = threadIdx.x;
   if ((int)blockIdx.x < n_conv_wg) {
-    // chunk idx = ((hq * T_q) + row) * (d/8) + c: reads the head-major
-    // accumulator in order, writes dq[row][hq][8c .. 8c+7]
-    const int64_t idx = (int64_t)blockIdx.x * 256 + tid;
-    if (idx >= n_chunks) return;
-    const int cpr = p.d / 8;
-    const int64_t hr = idx / cpr;
-    const int c8 = (int)(idx - hr * cpr) * 8;
-    const int64_t hq = hr / p.T_q;
-    const int64_t row = hr - hq * p.T_q;
-    const float* src = p.dq_acc + hr * DP + c8;
-    const f32x4 a = *(const f32x4*)src;
-    const f32x4 c = *(const f32x4*)(src + 4);
-    u32x4 out;
-    out[0] = (uint32_t)DT::bits(a[0] * p.scale) | ((uint32_t)DT::bits(a[1] * p.scale) << 16);
-    out[1] = (uint32_t)DT::bits(a[2] * p.scale) | ((uint32_t)DT::bits(a[3] * p.scale) << 16);
-    out[2] = (uint32_t)DT::bits(c[0] * p.scale) | ((uint32_t)DT::bits(c[1] * p.scale) << 16);
-    out[3] = (uint32_t)DT::bits(c[2] * p.scale) | ((uint32_t)DT::bits(c[3] * p.scale) << 16);
-    *(u32x4*)(p.dq + (row * p.h_q + hq) * p.d + c8) = out;
+    // (row, head) pairs in row-major order, like the pre pass: pair pr sits
+    // at pr * DP in the accumulator and at pr * d in dq, so each thread reads
+    // and writes chunk c of two pairs of one stream each.
+    constexpr int KCH = DP / 8, PB = kPairsPerBlock<DP>;
+    const int64_t pairs = p.T_q * p.h_q;
+    const int64_t p0 = (int64_t)blockIdx.x * PB;
+    const int g = tid / KCH;
+    const int c = tid % KCH;
+    if (8 * c >= p.d) return;
+    f32x4 v[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t pr = p0 + g + t * (PB / 2);
+      if (pr < pairs) {
+        const float* src = p.dq_acc + pr * DP + 8 * c;
+        v[t][0] = *(const f32x4*)src;
+        v[t][1] = *(const f32x4*)(src + 4);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int64_t pr = p0 + g + t * (PB / 2);
+      if (pr < pairs) {
+        u32x4 out;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const f32x4& x = v[t][k >> 1];
+          out[k] = (uint32_t)DT::bits(x[2 * (k & 1)] * p.scale) |
+                   ((uint32_t)DT::bits(x[2 * (k & 1) + 1] * p.scale) << 16);
+        }
+        *(u32x4*)(p.dq + pr * p.d + 8 * c) = out;
+      }
+    }
     return;
   }
   __shared__ uint8_t invalid[kZeroRowsB];
@@ -619,8 +656,8 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   };
   hipError_t em = mark(0);
   if (em != hipSuccess) return em;
-  const int64_t pairs = bp.T_q * bp.h_q;
-  const int64_t n_pre = bp.n_sched + (pairs + 15) / 16;
+  const int64_t n_pair_blocks = (bp.T_q * bp.h_q + kPairsPerBlock<DP> - 1) / kPairsPerBlock<DP>;
+  const int64_t n_pre = bp.n_sched + n_pair_blocks;
   if (n_pre > 0) {
     hipLaunchKernelGGL((thd_bwd_pre_kernel<DT, DP>), dim3((unsigned)n_pre), dim3(256), 0, s, bp);
     hipError_t e = hipGetLastError();
@@ -633,12 +670,11 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
     if (e != hipSuccess) return e;
   }
   if ((em = mark(2)) != hipSuccess) return em;
-  const int64_t n_chunks = bp.T_q * bp.h_q * bp.d / 8;
-  const int64_t n_conv = (n_chunks + 255) / 256;
+  const int64_t n_conv = n_pair_blocks;
   const int64_t n_zero = (bp.T_kv + kZeroRowsB - 1) / kZeroRowsB;
   if (n_conv + n_zero > 0) {
     hipLaunchKernelGGL((thd_bwd_post_kernel<DT, DP>), dim3((unsigned)(n_conv + n_zero)), dim3(256), 0,
-                       s, bp, n_chunks, (int)n_conv);
+                       s, bp, (int)n_conv);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
