@@ -73,6 +73,27 @@ def test_fwd_rejects_invalid_arguments(kw, status):
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, 1 << 30, None) == status
 
 
+def test_sequence_size_limits():
+    # 32-bit byte offsets per sequence: q / k / v rows of max_seqlen rows must
+    # stay below 2^31 bytes, and in the backward the fp32 dq accumulator rows
+    # (h_q * DP * 4 bytes) too.
+    lib = _lib.load()
+    fwd = lambda a: lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, P, 1 << 30, None)
+    bwd = lambda a: lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, 1 << 30, None)
+    big_q = dict(max_seqlen_q=(1 << 31) // (4 * 64 * 2), total_q=1 << 20)   # q rows hit 2^31
+    assert fwd(_args(**big_q)) == -2 and bwd(_args(**big_q)) == -2
+    big_kv = dict(max_seqlen_kv=(1 << 31) // (2 * 64 * 2), total_kv=1 << 21)
+    assert fwd(_args(**big_kv)) == -2 and bwd(_args(**big_kv)) == -2
+    # fits the forward's bf16 rows but not the backward's fp32 accumulator
+    acc_only = dict(max_seqlen_q=(1 << 31) // (4 * 64 * 4), total_q=1 << 20)
+    assert bwd(_args(**acc_only)) == -2
+    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**acc_only))) == 0
+    # the forward passes the size checks and stops at the (empty) workspace,
+    # before anything could be launched with the placeholder pointers
+    assert lib.thd_attn_fwd(ctypes.byref(_args(**acc_only)), P, P, P, P, P, P, 0, None) == -4
+    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(**acc_only))) > 0
+
+
 def test_null_and_misaligned_tensors():
     lib = _lib.load()
     a = _args()
