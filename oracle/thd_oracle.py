@@ -355,3 +355,48 @@ def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, mask_type=None,
             dqs.append(scale * (ds @ K[:n_vis]))
     dq = np.array(dqs) if dout is not None else None
     return np.array(outs), np.array(lses), dq
+
+
+# ---------------------------------------------------------------------------
+# Context parallelism (Megatron-LM issue "How to pad sequences that cannot be
+# evenly split in context parallelism (CP)?", question): a sequence split over
+# n ranks is padded to a multiple of 2n.  Reading (not on the pages): the
+# load-balanced split into 2n equal chunks, rank r taking chunks r and 2n-1-r,
+# pads at the end of the sequence.
+# ---------------------------------------------------------------------------
+def cp_padded_length(length, n):
+    """Rows of the padded sequence: the least multiple of 2n that holds it."""
+    return -(-int(length) // (2 * n)) * (2 * n)
+
+
+def cp_local_positions(length, n, r):
+    """Positions (0 .. padded length - 1) of the padded sequence held by rank
+    r, in its local order: chunk r, then chunk 2n-1-r."""
+    padded = cp_padded_length(length, n)
+    c = padded // (2 * n)
+    chunks = [r, 2 * n - 1 - r]
+    return [k * c + i for k in chunks for i in range(c)]
+
+
+def cp_attn_rank(q, k, v, lengths, n, r, mask_type=None, scale=None):
+    """Rank r's outputs by the definition: the full attention of every
+    sequence (``attn_fwd`` on the unsplit, unpadded sequences), read at the
+    positions rank r holds.  Returns (o [rows, h_q, d], lse [h_q, rows]) for
+    rank r's local rows, pad positions 0 / -inf.  q, k, v: [sum lengths, h, d]
+    packed without padding."""
+    lengths = [int(x) for x in lengths]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    o_full, lse_full = attn_fwd(q, k, v, cu, cu, len(lengths), mask_type=mask_type, scale=scale)
+    rows_o, rows_l = [], []
+    for b, length in enumerate(lengths):
+        for pos in cp_local_positions(length, n, r):
+            if pos < length:
+                rows_o.append(o_full[cu[b] + pos])
+                rows_l.append(lse_full[:, cu[b] + pos])
+            else:
+                rows_o.append(np.zeros_like(o_full[0]))
+                rows_l.append(np.full(lse_full.shape[0], -np.inf))
+    h = q.shape[1]
+    if not rows_o:
+        return np.zeros((0, h, q.shape[2])), np.zeros((h, 0))
+    return np.stack(rows_o), np.stack(rows_l, axis=1)

@@ -1,0 +1,127 @@
+"""Context parallelism, the share of one rank, on one GPU.
+
+Megatron-LM issue "How to pad sequences that cannot be evenly split in context
+parallelism (CP)?" (question and repro): a sequence split over n devices is
+padded to a multiple of 2n and the pad is marked with ``cu_seqlens_padded``.
+Here sequence b (valid length len_b) owns a global slot of P_b = 2n * C_b rows,
+C_b = ceil(len_b / 2n), valid rows first; it is cut into 2n chunks of C_b rows
+and rank r holds chunks r and 2n-1-r as one local slot.  Rank r's attention is
+the log-sum-exp merge of one forward per rank t (the KV ring), each on the views
+that ``thd_cp_layout`` describes; on one GPU every shard is local, so the ring's
+send/recv is replaced by reading the peer's shard in place.
+
+Everything here is argument marshalling; the layout, the gather, the attention
+steps and the merge run in libthdattn.so.
+"""
+import ctypes
+
+import torch
+
+from . import _lib
+from .attention import _ptr, _require_cuda, _stream, attn_fwd
+
+SIDE_Q = 0
+SIDE_KV = 1
+
+_DECLARED = set()
+
+
+def _lib_cp():
+    lib = _lib.load()
+    if id(lib) not in _DECLARED:
+        vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+        lib.thd_cp_layout.argtypes = [vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp, vp]
+        lib.thd_cp_layout.restype = ctypes.c_int
+        lib.thd_cp_gather.argtypes = [vp, vp, vp, i32, i32, i32, vp, i64, vp, i64, i32, vp]
+        lib.thd_cp_gather.restype = ctypes.c_int
+        lib.thd_attn_lse_merge.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
+        lib.thd_attn_lse_merge.restype = ctypes.c_int
+        _DECLARED.add(id(lib))
+    return lib
+
+
+def _opt(t):
+    return None if t is None else _ptr(t)
+
+
+def cp_layout(cu_seqlens, cp_size, rank, peer, side, *, mask_type=None, batch_size=None):
+    """Device metadata of one step's view (see thd_cp_layout in thd_attn.h).
+
+    Returns a dict of int32 tensors ``cu_seqlens``, ``cu_seqlens_padded``,
+    ``global_cu_seqlens_padded`` ([batch+1] each) and uint8 ``mask_type``
+    ([batch]).
+    """
+    _require_cuda("cu_seqlens", cu_seqlens, torch.int32)
+    b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
+    if mask_type is not None:
+        _require_cuda("mask_type", mask_type, torch.uint8)
+    dev = cu_seqlens.device
+    out = {k: torch.empty(b + 1, dtype=torch.int32, device=dev)
+           for k in ("cu_seqlens", "cu_seqlens_padded", "global_cu_seqlens_padded")}
+    out["mask_type"] = torch.empty(max(b, 1), dtype=torch.uint8, device=dev)
+    st = _lib_cp().thd_cp_layout(_ptr(cu_seqlens), _opt(mask_type), b, cp_size, rank, peer, side,
+                                 _ptr(out["cu_seqlens"]), _ptr(out["cu_seqlens_padded"]),
+                                 _ptr(out["global_cu_seqlens_padded"]), _ptr(out["mask_type"]),
+                                 _stream(dev))
+    _lib.check(st, "thd_cp_layout")
+    return out
+
+
+def cp_shard(x, cu_seqlens, cp_size, rank, total_local, *, batch_size=None, out=None):
+    """Rank ``rank``'s shard [total_local, ...] of ``x`` [T_padded, ...] (global
+    padded layout); ``total_local`` = T_padded / cp_size."""
+    _require_cuda("x", x)
+    own = cp_layout(cu_seqlens, cp_size, rank, rank, SIDE_Q, batch_size=batch_size)
+    b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
+    if out is None:
+        out = torch.zeros((total_local,) + tuple(x.shape[1:]), dtype=x.dtype, device=x.device)
+    row_bytes = x[0].numel() * x.element_size() if x.shape[0] else out[0].numel() * out.element_size()
+    st = _lib_cp().thd_cp_gather(_ptr(cu_seqlens), _ptr(own["cu_seqlens_padded"]),
+                                 _ptr(own["global_cu_seqlens_padded"]), b, cp_size, rank, _ptr(x),
+                                 x.shape[0], _ptr(out), total_local, row_bytes, _stream(x.device))
+    _lib.check(st, "thd_cp_gather")
+    return out
+
+
+def lse_merge(o_part, lse_part, o_acc, lse_acc, *, first, o_out=None):
+    """Fold (o_part, lse_part) into the fp32 accumulator (o_acc, lse_acc) in place."""
+    _require_cuda("o_part", o_part)
+    _require_cuda("o_acc", o_acc, torch.float32)
+    _require_cuda("lse_part", lse_part, torch.float32)
+    _require_cuda("lse_acc", lse_acc, torch.float32)
+    total, h, d = o_part.shape
+    dt = _lib.THD_BF16 if o_part.dtype == torch.bfloat16 else _lib.THD_FP16
+    st = _lib_cp().thd_attn_lse_merge(_ptr(o_part), _ptr(lse_part), _ptr(o_acc), _ptr(lse_acc),
+                                      _opt(o_out), total, h, d, dt, int(bool(first)),
+                                      _stream(o_part.device))
+    _lib.check(st, "thd_attn_lse_merge")
+
+
+def cp_attn_fwd(q_local, k_shards, v_shards, cu_seqlens, cp_size, rank, max_seqlen, *,
+                mask_type=None, softmax_scale=None, batch_size=None):
+    """Rank ``rank``'s attention output over its local queries.
+
+    ``q_local``: its query shard; ``k_shards`` / ``v_shards``: the key and value
+    shards of every rank (index = rank).  ``max_seqlen``: bound on the global
+    valid lengths.  Returns (out [T_local, h_q, d], lse [h_q, T_local] fp32).
+    """
+    n = int(cp_size)
+    b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
+    max_local = 2 * ((int(max_seqlen) + 2 * n - 1) // (2 * n))
+    T, hq, d = q_local.shape
+    o_acc = torch.empty((T, hq, d), dtype=torch.float32, device=q_local.device)
+    lse_acc = torch.empty((hq, T), dtype=torch.float32, device=q_local.device)
+    out = torch.empty_like(q_local)
+    o_step = torch.empty_like(q_local)
+    lse_step = torch.empty((hq, T), dtype=torch.float32, device=q_local.device)
+    for s in range(n):
+        t = (rank - s) % n  # the ring: step s reads the keys of rank r - s
+        vq = cp_layout(cu_seqlens, n, rank, t, SIDE_Q, mask_type=mask_type, batch_size=b)
+        vk = cp_layout(cu_seqlens, n, rank, t, SIDE_KV, mask_type=mask_type, batch_size=b)
+        attn_fwd(q_local, k_shards[t], v_shards[t], vq["cu_seqlens"], vk["cu_seqlens"],
+                 max_local, max_local, cu_seqlens_q_padded=vq["cu_seqlens_padded"],
+                 cu_seqlens_kv_padded=vk["cu_seqlens_padded"], mask_type=vq["mask_type"][:b],
+                 softmax_scale=softmax_scale, batch_size=b, out=o_step, lse=lse_step)
+        lse_merge(o_step, lse_step, o_acc, lse_acc, first=(s == 0),
+                  o_out=out if s == n - 1 else None)
+    return out, lse_acc

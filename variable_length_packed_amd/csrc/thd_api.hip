@@ -176,4 +176,50 @@ int thd_attn_bwd_timed(const thd_varlen_args* args, const void* q, const void* k
                        stream, events);
 }
 
+int thd_cp_layout(const int32_t* cu_seqlens, const uint8_t* mask_type, int32_t batch,
+                  int32_t cp_size, int32_t rank, int32_t peer, int32_t side,
+                  int32_t* out_cu_seqlens, int32_t* out_cu_seqlens_padded,
+                  int32_t* out_global_cu_seqlens_padded, uint8_t* out_mask_type, void* stream) {
+  if (batch < 0 || cp_size < 1 || rank < 0 || rank >= cp_size || peer < 0 || peer >= cp_size ||
+      (side != 0 && side != 1))
+    return THD_ERR_SHAPE;
+  if (!cu_seqlens) return THD_ERR_NULL;
+  thd::CpLayoutArgs a{cu_seqlens, mask_type, batch, cp_size, rank, peer, side,
+                      out_cu_seqlens, out_cu_seqlens_padded, out_global_cu_seqlens_padded,
+                      out_mask_type};
+  return thd::launch_cp_layout(a, (hipStream_t)stream) == hipSuccess ? THD_OK : THD_ERR_HIP;
+}
+
+int thd_cp_gather(const int32_t* cu_seqlens, const int32_t* local_cu_seqlens_padded,
+                  const int32_t* global_cu_seqlens_padded, int32_t batch, int32_t cp_size,
+                  int32_t rank, const void* src, int64_t total_global, void* dst,
+                  int64_t total_local, int32_t row_bytes, void* stream) {
+  if (batch < 0 || cp_size < 1 || rank < 0 || rank >= cp_size || total_global < 0 ||
+      total_local < 0 || row_bytes <= 0 || row_bytes % 16 != 0)
+    return THD_ERR_SHAPE;
+  if (batch == 0 || total_local == 0) return THD_OK;
+  if (!cu_seqlens || !local_cu_seqlens_padded || !global_cu_seqlens_padded || !dst ||
+      (total_global > 0 && !src))
+    return THD_ERR_NULL;
+  if (!aligned16(dst) || (src && !aligned16(src))) return THD_ERR_UNSUPPORTED;
+  thd::CpGatherArgs a{cu_seqlens, local_cu_seqlens_padded, global_cu_seqlens_padded, batch,
+                      cp_size, rank, src, total_global, dst, total_local, row_bytes};
+  return thd::launch_cp_gather(a, (hipStream_t)stream) == hipSuccess ? THD_OK : THD_ERR_HIP;
+}
+
+int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, float* lse_acc,
+                       void* o_out, int64_t total, int32_t h, int32_t head_dim, int32_t dtype,
+                       int32_t first, void* stream) {
+  if (total < 0 || h <= 0 || head_dim <= 0 || head_dim % 8 != 0) return THD_ERR_SHAPE;
+  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
+  if (total == 0) return THD_OK;
+  if (!o_part || !lse_part || !o_acc || !lse_acc) return THD_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(o_acc) || (o_out && !aligned16(o_out)))
+    return THD_ERR_UNSUPPORTED;
+  thd::MergeArgs a{o_part, lse_part, o_acc, lse_acc, o_out, total, h, head_dim, first != 0};
+  return thd::launch_lse_merge(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
+             ? THD_OK
+             : THD_ERR_HIP;
+}
+
 }  // extern "C"

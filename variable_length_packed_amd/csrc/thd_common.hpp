@@ -129,12 +129,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // synchronises the workgroup before the tile is read.  Written as assembly:
 // the compiler cannot tell the tile being filled from the tiles being read
 // and would otherwise wait for the load before every transpose read of LDS.
+// M0 is otherwise unused by these kernels (no compiler-generated instruction
+// reads or writes it; checked in the generated code), so the clobber is safe.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void buf_load_lds16(u32x4 rs, uint32_t lds_wave, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds_wave)), "v"(voff), "s"(rs)
                : "m0", "memory");
 }
+#pragma clang diagnostic pop
 
 __device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, 0);
