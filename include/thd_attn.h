@@ -232,6 +232,17 @@ int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, 
                        void* o_out, int64_t total, int32_t h, int32_t head_dim, int32_t dtype,
                        int32_t first, void* stream);
 
+/* Sum of partial gradients in fp32: acc[i] += src[i] for i < n_elems (first
+ * != 0: acc[i] = src[i]), src in the storage dtype; out (may be NULL) also
+ * receives the sum in the storage dtype (RNE).  Rank r's gradients are the
+ * sums of one thd_attn_bwd per ring step (on the step's views, with the
+ * merged o and lse of its queries): dq over the steps, and the dk / dv
+ * contributions to each rank's shard over the ranks.  n_elems: a multiple of
+ * 8; pointers 16-byte aligned.  Errors: THD_ERR_SHAPE, THD_ERR_UNSUPPORTED
+ * (dtype, alignment), THD_ERR_NULL, THD_ERR_HIP. */
+int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int32_t dtype,
+                   int32_t first, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -166,3 +166,68 @@ def test_cp_page_example_two_devices():
                 assert np.all(oc[j] == 0)
                 continue
             assert {"%.4f" % t for t in oc[j, 0]} == {gold["rows_0_3"] if pos < 4 else gold["rows_4_6"]}
+
+
+BWD_CASES = [
+    dict(seed=411, n=2, batch=5, max_len=300, h_q=2, h_kv=2, d=128, dtype="bf16", causal="mixed"),
+    dict(seed=412, n=4, batch=4, max_len=500, h_q=4, h_kv=2, d=64, dtype="bf16", causal="all"),
+    dict(seed=413, n=3, batch=5, max_len=200, h_q=2, h_kv=1, d=128, dtype="fp16", causal="none"),
+]
+
+
+@pytest.mark.parametrize("c", BWD_CASES, ids=[f"cp{c['n']}_{c['seed']}" for c in BWD_CASES])
+def test_cp_backward_matches_full_attention(c):
+    """Each rank's dq, and every shard's dk / dv summed over the ranks'
+    contributions, equal the full backward at the shard's rows."""
+    n = c["n"]
+    lengths = _lengths(c["seed"], c["batch"], c["max_len"], n)
+    k = len(lengths)
+    causal = {"none": np.zeros(k), "all": np.ones(k),
+              "mixed": (np.arange(k) % 2 == 0)}[c["causal"]].astype(np.uint8)
+    print(f"case {c}", flush=True)
+    rng = torch.Generator().manual_seed(c["seed"])
+    tot = int(np.sum(lengths))
+    dt = DT[c["dtype"]]
+    qp = torch.randn((tot, c["h_q"], c["d"]), generator=rng).to(dt)
+    kp = torch.randn((tot, c["h_kv"], c["d"]), generator=rng).to(dt)
+    vp = torch.randn((tot, c["h_kv"], c["d"]), generator=rng).to(dt)
+    dop = torch.randn((tot, c["h_q"], c["d"]), generator=rng).to(dt)
+    g = _global_layout(lengths, n)
+    T = int(g[-1])
+    cu_p = np.concatenate([[0], np.cumsum(lengths)])
+    glob = []
+    for x in (qp, kp, vp, dop):
+        y = torch.full((T,) + tuple(x.shape[1:]), 100.0, dtype=x.dtype)
+        for b, L in enumerate(lengths):
+            y[g[b]:g[b] + L] = x[cu_p[b]:cu_p[b] + L]
+        glob.append(y.cuda())
+    cu_g = _i32(cu_p)
+    mt = torch.from_numpy(causal).cuda()
+    q_s, k_s, v_s, do_s = ([cp.cp_shard(t, cu_g, n, r, T // n) for r in range(n)] for t in glob)
+    parts, dqs = [], []
+    for r in range(n):
+        o, lse = cp.cp_attn_fwd(q_s[r], k_s, v_s, cu_g, n, r, max(lengths), mask_type=mt)
+        dq, pr = cp.cp_attn_bwd(q_s[r], k_s, v_s, o, do_s[r], lse, cu_g, n, r, max(lengths),
+                                mask_type=mt)
+        dqs.append(dq)
+        parts.append(pr)
+    rdq, rdk, rdv = orc.attn_bwd(f64(qp), f64(kp), f64(vp), f64(dop), cu_p, cu_p, k,
+                                 mask_type=causal)
+
+    def at_rank(full, r):
+        rows = []
+        for b, L in enumerate(lengths):
+            for pos in orc.cp_local_positions(L, n, r):
+                rows.append(full[cu_p[b] + pos] if pos < L else np.zeros_like(full[0]))
+        return np.stack(rows)
+
+    for r in range(n):
+        valid = np.array([p < L for L in lengths for p in orc.cp_local_positions(L, n, r)])
+        assert_close(f"rank {r} dq", f64(dqs[r])[valid], at_rank(rdq, r)[valid], c["dtype"])
+        dk = cp.cp_reduce([parts[s][r][0] for s in range(n)])
+        dv = cp.cp_reduce([parts[s][r][1] for s in range(n)])
+        assert_close(f"shard {r} dk", f64(dk)[valid], at_rank(rdk, r)[valid], c["dtype"])
+        assert_close(f"shard {r} dv", f64(dv)[valid], at_rank(rdv, r)[valid], c["dtype"])
+        for name, t in (("dq", dqs[r]), ("dk", dk), ("dv", dv)):
+            bits = t.detach().view(torch.int16).cpu().numpy()[~valid]
+            assert np.all(bits == 0), f"rank {r} {name}: nonzero pad rows"

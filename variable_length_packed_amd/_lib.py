@@ -34,6 +34,7 @@ EXPORTED = (
     "thd_cp_layout",
     "thd_cp_gather",
     "thd_attn_lse_merge",
+    "thd_accumulate",
     "thd_status_string",
     "thd_version",
 )

@@ -10,15 +10,21 @@ the log-sum-exp merge of one forward per rank t (the KV ring), each on the views
 that ``thd_cp_layout`` describes; on one GPU every shard is local, so the ring's
 send/recv is replaced by reading the peer's shard in place.
 
+The backward of rank r is one attention backward per ring step on the same
+views, with the merged output and log-sum-exp of its queries: the dq of the
+steps add up to rank r's dq, and each step's dk / dv is rank r's contribution
+to the shard of the rank whose keys it read (in a ring they travel back to that
+rank, which sums what every rank sends).  Sums are fp32.
+
 Everything here is argument marshalling; the layout, the gather, the attention
-steps and the merge run in libthdattn.so.
+steps, the merge and the sums run in libthdattn.so.
 """
 import ctypes
 
 import torch
 
 from . import _lib
-from .attention import _ptr, _require_cuda, _stream, attn_fwd
+from .attention import _ptr, _require_cuda, _stream, attn_bwd, attn_fwd
 
 SIDE_Q = 0
 SIDE_KV = 1
@@ -36,6 +42,8 @@ def _lib_cp():
         lib.thd_cp_gather.restype = ctypes.c_int
         lib.thd_attn_lse_merge.argtypes = [vp, vp, vp, vp, vp, i64, i32, i32, i32, i32, vp]
         lib.thd_attn_lse_merge.restype = ctypes.c_int
+        lib.thd_accumulate.argtypes = [vp, vp, vp, i64, i32, i32, vp]
+        lib.thd_accumulate.restype = ctypes.c_int
         _DECLARED.add(id(lib))
     return lib
 
@@ -125,3 +133,53 @@ def cp_attn_fwd(q_local, k_shards, v_shards, cu_seqlens, cp_size, rank, max_seql
         lse_merge(o_step, lse_step, o_acc, lse_acc, first=(s == 0),
                   o_out=out if s == n - 1 else None)
     return out, lse_acc
+
+
+def accumulate(src, acc, *, first, out=None):
+    """acc (+)= src in fp32 (first: =); out, if given, receives the sum in src's dtype."""
+    _require_cuda("src", src)
+    _require_cuda("acc", acc, torch.float32)
+    if acc.numel() != src.numel() or (out is not None and out.numel() != src.numel()):
+        raise ValueError("accumulate: sizes differ")
+    dt = _lib.THD_BF16 if src.dtype == torch.bfloat16 else _lib.THD_FP16
+    st = _lib_cp().thd_accumulate(_ptr(src), _ptr(acc), _opt(out), src.numel(), dt,
+                                  int(bool(first)), _stream(src.device))
+    _lib.check(st, "thd_accumulate")
+
+
+def cp_attn_bwd(q_local, k_shards, v_shards, out_local, dout_local, lse_local, cu_seqlens,
+                cp_size, rank, max_seqlen, *, mask_type=None, softmax_scale=None,
+                batch_size=None):
+    """Rank ``rank``'s backward.  ``out_local`` / ``lse_local``: its merged
+    forward outputs (``cp_attn_fwd``).  Returns (dq [T_local, h_q, d], parts):
+    parts[t] = (dk, dv) of rank t's key shard contributed by this rank's
+    queries, in the storage dtype (the shard's owner sums them with
+    ``cp_reduce``)."""
+    n = int(cp_size)
+    b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
+    max_local = 2 * ((int(max_seqlen) + 2 * n - 1) // (2 * n))
+    dq_acc = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
+    dq = torch.empty_like(q_local)
+    parts = [None] * n
+    for s in range(n):
+        t = (rank - s) % n
+        vq = cp_layout(cu_seqlens, n, rank, t, SIDE_Q, mask_type=mask_type, batch_size=b)
+        vk = cp_layout(cu_seqlens, n, rank, t, SIDE_KV, mask_type=mask_type, batch_size=b)
+        dq_s, dk_s, dv_s = attn_bwd(
+            q_local, k_shards[t], v_shards[t], out_local, dout_local, lse_local,
+            vq["cu_seqlens"], vk["cu_seqlens"], max_local, max_local,
+            cu_seqlens_q_padded=vq["cu_seqlens_padded"], cu_seqlens_kv_padded=vk["cu_seqlens_padded"],
+            mask_type=vq["mask_type"][:b], softmax_scale=softmax_scale, batch_size=b)
+        accumulate(dq_s, dq_acc, first=(s == 0), out=dq if s == n - 1 else None)
+        parts[t] = (dk_s, dv_s)
+    return dq, parts
+
+
+def cp_reduce(parts):
+    """Sum of the contributions to one shard (a list of same-shaped tensors) in
+    fp32, returned in their dtype."""
+    acc = torch.empty(parts[0].shape, dtype=torch.float32, device=parts[0].device)
+    out = torch.empty_like(parts[0])
+    for i, p in enumerate(parts):
+        accumulate(p, acc, first=(i == 0), out=out if i == len(parts) - 1 else None)
+    return out

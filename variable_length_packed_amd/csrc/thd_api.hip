@@ -222,4 +222,17 @@ int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, 
              : THD_ERR_HIP;
 }
 
+int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int32_t dtype,
+                   int32_t first, void* stream) {
+  if (n_elems < 0 || n_elems % 8 != 0) return THD_ERR_SHAPE;
+  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
+  if (n_elems == 0) return THD_OK;
+  if (!src || !acc) return THD_ERR_NULL;
+  if (!aligned16(src) || !aligned16(acc) || (out && !aligned16(out))) return THD_ERR_UNSUPPORTED;
+  thd::AccumulateArgs a{src, acc, out, n_elems, first != 0};
+  return thd::launch_accumulate(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
+             ? THD_OK
+             : THD_ERR_HIP;
+}
+
 }  // extern "C"

@@ -209,7 +209,41 @@ __global__ __launch_bounds__(256) void thd_lse_merge_kernel(MergeArgs a) {
   if (c == 0) a.lse_acc[li] = lse;
 }
 
+// acc (+)= src elementwise in fp32 (first: =), 8 elements per thread; with
+// out, the sum is also written in the storage dtype.
+template <class DT>
+__global__ __launch_bounds__(256) void thd_accumulate_kernel(AccumulateArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= a.n) return;
+  const u32x4 v = *(const u32x4*)((const uint16_t*)a.src + i);
+  float* acc = a.acc + i;
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float x = DT::to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+    o[e] = a.first ? x : acc[e] + x;
+    acc[e] = o[e];
+  }
+  if (a.out) {
+    u32x4 w;
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)DT::bits(o[2 * k]) | ((uint32_t)DT::bits(o[2 * k + 1]) << 16);
+    *(u32x4*)((uint16_t*)a.out + i) = w;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_accumulate(const AccumulateArgs& a, bool bf16, hipStream_t s) {
+  if (a.n == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((a.n / 8 + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(thd_accumulate_kernel<Bf16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(thd_accumulate_kernel<Fp16>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_cp_layout(const CpLayoutArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(thd_cp_layout_kernel, dim3(1), dim3(256), 0, s, a);

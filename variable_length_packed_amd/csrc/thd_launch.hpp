@@ -84,6 +84,15 @@ struct MergeArgs {
   int first;
 };
 
+struct AccumulateArgs {
+  const void* src;  // n elements, storage dtype
+  float* acc;       // n elements
+  void* out;        // may be null
+  int64_t n;        // multiple of 8
+  int first;
+};
+
+hipError_t launch_accumulate(const AccumulateArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_cp_layout(const CpLayoutArgs& a, hipStream_t s);
 hipError_t launch_cp_gather(const CpGatherArgs& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, bool bf16, hipStream_t s);
