@@ -105,8 +105,22 @@ def lse_merge(o_part, lse_part, o_acc, lse_acc, *, first, o_out=None):
     _lib.check(st, "thd_attn_lse_merge")
 
 
+def cp_views(cu_seqlens, cp_size, rank, *, mask_type=None, batch_size=None):
+    """The (query view, key view) of every ring step of rank ``rank``, in ring
+    order (step s reads the keys of rank (rank - s) mod cp_size)."""
+    n = int(cp_size)
+    out = []
+    for s in range(n):
+        t = (rank - s) % n
+        out.append((t, cp_layout(cu_seqlens, n, rank, t, SIDE_Q, mask_type=mask_type,
+                                 batch_size=batch_size),
+                    cp_layout(cu_seqlens, n, rank, t, SIDE_KV, mask_type=mask_type,
+                              batch_size=batch_size)))
+    return out
+
+
 def cp_attn_fwd(q_local, k_shards, v_shards, cu_seqlens, cp_size, rank, max_seqlen, *,
-                mask_type=None, softmax_scale=None, batch_size=None):
+                mask_type=None, softmax_scale=None, batch_size=None, views=None):
     """Rank ``rank``'s attention output over its local queries.
 
     ``q_local``: its query shard; ``k_shards`` / ``v_shards``: the key and value
@@ -122,10 +136,8 @@ def cp_attn_fwd(q_local, k_shards, v_shards, cu_seqlens, cp_size, rank, max_seql
     out = torch.empty_like(q_local)
     o_step = torch.empty_like(q_local)
     lse_step = torch.empty((hq, T), dtype=torch.float32, device=q_local.device)
-    for s in range(n):
-        t = (rank - s) % n  # the ring: step s reads the keys of rank r - s
-        vq = cp_layout(cu_seqlens, n, rank, t, SIDE_Q, mask_type=mask_type, batch_size=b)
-        vk = cp_layout(cu_seqlens, n, rank, t, SIDE_KV, mask_type=mask_type, batch_size=b)
+    views = views or cp_views(cu_seqlens, n, rank, mask_type=mask_type, batch_size=b)
+    for s, (t, vq, vk) in enumerate(views):
         attn_fwd(q_local, k_shards[t], v_shards[t], vq["cu_seqlens"], vk["cu_seqlens"],
                  max_local, max_local, cu_seqlens_q_padded=vq["cu_seqlens_padded"],
                  cu_seqlens_kv_padded=vk["cu_seqlens_padded"], mask_type=vq["mask_type"][:b],
@@ -149,7 +161,7 @@ def accumulate(src, acc, *, first, out=None):
 
 def cp_attn_bwd(q_local, k_shards, v_shards, out_local, dout_local, lse_local, cu_seqlens,
                 cp_size, rank, max_seqlen, *, mask_type=None, softmax_scale=None,
-                batch_size=None):
+                batch_size=None, views=None):
     """Rank ``rank``'s backward.  ``out_local`` / ``lse_local``: its merged
     forward outputs (``cp_attn_fwd``).  Returns (dq [T_local, h_q, d], parts):
     parts[t] = (dk, dv) of rank t's key shard contributed by this rank's
@@ -161,10 +173,8 @@ def cp_attn_bwd(q_local, k_shards, v_shards, out_local, dout_local, lse_local, c
     dq_acc = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
     dq = torch.empty_like(q_local)
     parts = [None] * n
-    for s in range(n):
-        t = (rank - s) % n
-        vq = cp_layout(cu_seqlens, n, rank, t, SIDE_Q, mask_type=mask_type, batch_size=b)
-        vk = cp_layout(cu_seqlens, n, rank, t, SIDE_KV, mask_type=mask_type, batch_size=b)
+    views = views or cp_views(cu_seqlens, n, rank, mask_type=mask_type, batch_size=b)
+    for s, (t, vq, vk) in enumerate(views):
         dq_s, dk_s, dv_s = attn_bwd(
             q_local, k_shards[t], v_shards[t], out_local, dout_local, lse_local,
             vq["cu_seqlens"], vk["cu_seqlens"], max_local, max_local,
