@@ -189,16 +189,21 @@ __global__ __launch_bounds__(256) void thd_lse_merge_kernel(MergeArgs a) {
     wa *= inv;
     wb *= inv;
   }
-  float* acc = a.o_acc + pr * a.d + 8 * c;
+  f32x4* acc = (f32x4*)(a.o_acc + pr * a.d + 8 * c);
   const u32x4 pv = *(const u32x4*)((const uint16_t*)a.o_part + pr * a.d + 8 * c);
+  f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (!a.first) {
+    y[0] = acc[0];
+    y[1] = acc[1];
+  }
   float o[8];
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
     const float x = DT::to_f32((uint16_t)(pv[e >> 1] >> (16 * (e & 1))));
-    const float y = a.first ? 0.f : acc[e];
-    o[e] = wa * y + wb * x;
-    acc[e] = o[e];
+    o[e] = wa * y[e >> 2][e & 3] + wb * x;
   }
+  acc[0] = f32x4{o[0], o[1], o[2], o[3]};
+  acc[1] = f32x4{o[4], o[5], o[6], o[7]};
   if (a.o_out) {
     u32x4 out;
 #pragma unroll
@@ -216,14 +221,18 @@ __global__ __launch_bounds__(256) void thd_accumulate_kernel(AccumulateArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
   if (i >= a.n) return;
   const u32x4 v = *(const u32x4*)((const uint16_t*)a.src + i);
-  float* acc = a.acc + i;
+  f32x4* acc = (f32x4*)(a.acc + i);
+  f32x4 y[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (!a.first) {
+    y[0] = acc[0];
+    y[1] = acc[1];
+  }
   float o[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const float x = DT::to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
-    o[e] = a.first ? x : acc[e] + x;
-    acc[e] = o[e];
-  }
+  for (int e = 0; e < 8; ++e)
+    o[e] = y[e >> 2][e & 3] + DT::to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+  acc[0] = f32x4{o[0], o[1], o[2], o[3]};
+  acc[1] = f32x4{o[4], o[5], o[6], o[7]};
   if (a.out) {
     u32x4 w;
 #pragma unroll
