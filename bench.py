@@ -206,17 +206,18 @@ def main():
                                           P["lse"], P["dq"], P["dk"], P["dv"], P["ws"],
                                           ws_bytes, stream, ev_arrays[i]), "bwd")
 
-    def untimed_step():
-        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], stream),
+    def untimed_step(st=None):
+        st = stream if st is None else st
+        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], st),
                    "mask q")
-        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
+        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], st),
                    "mask kv")
         _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
-                                    fws_bytes, stream), "fwd")
+                                    fws_bytes, st), "fwd")
         if a.fwd_only:
             return
         _lib.check(lib.thd_attn_bwd(args, P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"],
-                                    P["dq"], P["dk"], P["dv"], P["ws"], ws_bytes, stream), "bwd")
+                                    P["dq"], P["dk"], P["dv"], P["ws"], ws_bytes, st), "bwd")
 
     t_spin = time.perf_counter()
     while time.perf_counter() - t_spin < a.spinup_seconds:
@@ -232,9 +233,42 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # The same step captured once in a HIP graph and replayed: the launches of
+    # the eager step above cost host time between kernels, a replay does not.
+    # (Reported beside the eager figures; a capture failure only drops it.)
+    def graph_time():
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)  # default priority
+        side.wait_stream(cur)
+        with torch.cuda.stream(side):
+            untimed_step(_stream(dev))
+        cur.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            untimed_step(_stream(dev))   # the capture stream
+        torch.cuda.synchronize()
+        for _ in range(a.warmup):
+            g.replay()
+        torch.cuda.synchronize()
+        g0, g1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        g0.record(cur)
+        for _ in range(a.steps):
+            g.replay()
+        g1.record(cur)
+        torch.cuda.synchronize()
+        return g0.elapsed_time(g1) / a.steps
+
+    try:
+        graph_ms = graph_time()
+    except Exception as e:  # pragma: no cover - reported, not fatal
+        print(f"bench.py: graph replay not measured: {e}", file=sys.stderr)
+        graph_ms = None
+
     timed = events[a.warmup:]
     if a.fwd_only:
-        print(json.dumps(fwd_only_result(a, w, timed, elapsed)), flush=True)
+        res = fwd_only_result(a, w, timed, elapsed)
+        res["graph_replay_ms_per_step"] = None if graph_ms is None else round(graph_ms, 4)
+        print(json.dumps(res), flush=True)
         return
     fwd_ms = [e[0].elapsed_time(e[1]) for e in timed]
     pre_ms = [e[2].elapsed_time(e[3]) for e in timed]
@@ -278,6 +312,10 @@ def main():
         "value_no_recompute_credit": round(value * 12 / 14, 2),
         "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 4),
                            "min": round(step_ms[0], 4)},
+        # the same step replayed from one HIP graph (no launch gaps)
+        "graph_replay": None if graph_ms is None else {
+            "ms_per_step": round(graph_ms, 4),
+            "value": round(flops / (graph_ms * 1e-3) / 1e12, 2)},
         "config": {
             "workload": (f"packed thd {'self-' if w.self_attention else 'cross-'}attention, "
                          f"config {w.name}: {w.batch} sequences, {w.T_q} query tokens"
