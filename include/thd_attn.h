@@ -243,6 +243,32 @@ int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, 
 int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int32_t dtype,
                    int32_t first, void* stream);
 
+/* The log-sum-exp merge of n_parts (1..8) partial attention outputs in one
+ * pass: with l_k = lse_parts[k] (natural log, [h, total]) and
+ * m = max_k l_k per (row, head), lse_out = m + log(sum_k e^(l_k - m)) and
+ * o_out = sum_k e^(l_k - lse_out) o_parts[k], in fp32, o_out written once in
+ * the storage dtype (RNE).  A (row, head) whose partials are all -inf gets
+ * lse -inf and o = 0.  o_parts[k] and o_out are [total, h, head_dim], 16-byte
+ * aligned; lse_out may be NULL; o_out may not alias a partial.  This is how
+ * rank r's output is formed from the forwards of its ring steps: reading
+ * each step's output once, against twice per step for the fp32 accumulator
+ * of thd_attn_lse_merge.  Errors: THD_ERR_SHAPE (total < 0, h <= 0,
+ * head_dim not a positive multiple of 8, n_parts outside 1..8),
+ * THD_ERR_UNSUPPORTED (dtype, alignment), THD_ERR_NULL, THD_ERR_HIP. */
+int thd_attn_lse_merge_n(const void* const* o_parts, const float* const* lse_parts,
+                         int32_t n_parts, void* o_out, float* lse_out, int64_t total, int32_t h,
+                         int32_t head_dim, int32_t dtype, void* stream);
+
+/* out[i] = sum_k parts[k][i] for i < n_elems, over n_parts (1..8) partials in
+ * the storage dtype, added in fp32 in the order given and written once in the
+ * storage dtype (RNE): the one-pass form of thd_accumulate, for rank r's dq
+ * over its ring steps and a shard's dk / dv over the ranks.  n_elems: a
+ * multiple of 8; pointers 16-byte aligned; out may not alias a partial.
+ * Errors: THD_ERR_SHAPE, THD_ERR_UNSUPPORTED (dtype, alignment),
+ * THD_ERR_NULL, THD_ERR_HIP. */
+int thd_sum_n(const void* const* parts, int32_t n_parts, void* out, int64_t n_elems,
+              int32_t dtype, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

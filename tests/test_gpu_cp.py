@@ -231,3 +231,73 @@ def test_cp_backward_matches_full_attention(c):
         for name, t in (("dq", dqs[r]), ("dk", dk), ("dv", dv)):
             bits = t.detach().view(torch.int16).cpu().numpy()[~valid]
             assert np.all(bits == 0), f"rank {r} {name}: nonzero pad rows"
+
+
+def _merge_reference(os_, ls_):
+    """The log-sum-exp merge written out in fp64: lse = log sum_k e^(l_k),
+    o = sum_k e^(l_k - lse) o_k; rows whose l_k are all -inf give -inf and 0."""
+    L = np.stack([l.astype(np.float64) for l in ls_])          # [n, h, T]
+    m = L.max(axis=0)
+    fin = np.isfinite(m)
+    w = np.where(np.isfinite(L), np.exp(L - np.where(fin, m, 0.0)), 0.0)
+    s = w.sum(axis=0)
+    lse = np.where(fin, np.where(fin, m, 0.0) + np.log(np.where(fin, s, 1.0)), -np.inf)
+    wn = np.where(fin, w / np.where(fin, s, 1.0), 0.0)          # [n, h, T]
+    o = sum(wn[k].T[:, :, None] * os_[k].astype(np.float64) for k in range(len(os_)))
+    return o, lse
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 5, 8])
+def test_lse_merge_n_matches_definition(n):
+    print(f"lse_merge_n: {n} partials", flush=True)
+    g = torch.Generator().manual_seed(300 + n)
+    T, h, d = 97, 3, 128
+    os_ = [torch.randn((T, h, d), generator=g).to(torch.bfloat16) for _ in range(n)]
+    ls_ = [4 * torch.randn((h, T), generator=g) for _ in range(n)]
+    for k in range(n):              # some partials see no key: -inf
+        ls_[k][:, (torch.arange(T) + k) % 5 == 0] = -float("inf")
+    ls_[0][:, 3] = -float("inf")    # row 3: -inf in every partial when n == 1
+    if n > 1:
+        for l in ls_:
+            l[:, 7] = -float("inf")  # row 7: -inf in every partial
+    for k in range(n):              # a partial that saw no key has o = 0
+        os_[k] = torch.where(torch.isinf(ls_[k]).T[:, :, None], torch.zeros_like(os_[k]),
+                             os_[k]).contiguous()
+    ro, rl = _merge_reference([o.float().numpy() for o in os_], [l.numpy() for l in ls_])
+    out, lse = cp.lse_merge_n([o.cuda() for o in os_], [l.cuda() for l in ls_])
+    fin = np.isfinite(rl)
+    assert np.array_equal(np.isfinite(lse.cpu().numpy()), fin)
+    assert np.abs(lse.cpu().numpy()[fin] - rl[fin]).max() < 1e-5
+    got = out.float().cpu().numpy()
+    # one rounding to bf16 of an fp32 sum of at most 8 weighted terms
+    assert np.all(np.abs(got - ro) <= 2 ** -8 * np.abs(ro) + 1e-6)
+    assert np.all(got.transpose(1, 0, 2)[~fin] == 0)
+    # the step-by-step fp32 accumulator merge agrees with the same definition
+    o_acc = torch.empty((T, h, d), dtype=torch.float32, device="cuda")
+    l_acc = torch.empty((h, T), dtype=torch.float32, device="cuda")
+    out2 = torch.empty_like(out)
+    for k in range(n):
+        cp.lse_merge(os_[k].cuda(), ls_[k].cuda(), o_acc, l_acc, first=(k == 0),
+                     o_out=out2 if k == n - 1 else None)
+    got2 = out2.float().cpu().numpy()
+    assert np.all(np.abs(got2 - ro) <= 2 ** -7 * np.abs(ro) + 1e-6)
+    assert np.abs(l_acc.cpu().numpy()[fin] - rl[fin]).max() < 1e-5
+
+
+@pytest.mark.parametrize("n", [1, 2, 4, 8])
+def test_sum_n_is_the_fp32_sum(n):
+    print(f"sum_n: {n} partials", flush=True)
+    g = torch.Generator().manual_seed(400 + n)
+    parts = [torch.randn((61, 4, 64), generator=g).to(torch.bfloat16) for _ in range(n)]
+    acc = torch.zeros(parts[0].shape, dtype=torch.float32)
+    for p in parts:                 # fp32, in the order given, one rounding
+        acc = acc + p.float()
+    want = acc.to(torch.bfloat16)
+    got = cp.sum_n([p.cuda() for p in parts]).cpu()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    # the fp32 accumulator form gives the same bits
+    a = torch.empty(parts[0].shape, dtype=torch.float32, device="cuda")
+    out = torch.empty_like(parts[0], device="cuda")
+    for k, p in enumerate(parts):
+        cp.accumulate(p.cuda(), a, first=(k == 0), out=out if k == n - 1 else None)
+    assert torch.equal(out.cpu().view(torch.int16), want.view(torch.int16))

@@ -35,6 +35,8 @@ EXPORTED = (
     "thd_cp_gather",
     "thd_attn_lse_merge",
     "thd_accumulate",
+    "thd_attn_lse_merge_n",
+    "thd_sum_n",
     "thd_status_string",
     "thd_version",
 )

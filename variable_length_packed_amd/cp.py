@@ -14,7 +14,9 @@ The backward of rank r is one attention backward per ring step on the same
 views, with the merged output and log-sum-exp of its queries: the dq of the
 steps add up to rank r's dq, and each step's dk / dv is rank r's contribution
 to the shard of the rank whose keys it read (in a ring they travel back to that
-rank, which sums what every rank sends).  Sums are fp32.
+rank, which sums what every rank sends).  Sums are fp32.  Up to 8 steps, the
+merge and the sums read every step's result once (thd_attn_lse_merge_n,
+thd_sum_n); beyond that they go through an fp32 accumulator step by step.
 
 Everything here is argument marshalling; the layout, the gather, the attention
 steps, the merge and the sums run in libthdattn.so.
@@ -44,6 +46,10 @@ def _lib_cp():
         lib.thd_attn_lse_merge.restype = ctypes.c_int
         lib.thd_accumulate.argtypes = [vp, vp, vp, i64, i32, i32, vp]
         lib.thd_accumulate.restype = ctypes.c_int
+        lib.thd_attn_lse_merge_n.argtypes = [vp, vp, i32, vp, vp, i64, i32, i32, i32, vp]
+        lib.thd_attn_lse_merge_n.restype = ctypes.c_int
+        lib.thd_sum_n.argtypes = [vp, i32, vp, i64, i32, vp]
+        lib.thd_sum_n.restype = ctypes.c_int
         _DECLARED.add(id(lib))
     return lib
 
@@ -105,6 +111,50 @@ def lse_merge(o_part, lse_part, o_acc, lse_acc, *, first, o_out=None):
     _lib.check(st, "thd_attn_lse_merge")
 
 
+MAX_PARTS = 8  # partials one thd_attn_lse_merge_n / thd_sum_n call takes
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+
+def lse_merge_n(o_parts, lse_parts, *, out=None, lse_out=None):
+    """One-pass log-sum-exp merge of up to 8 partial outputs (storage dtype)
+    and their lse ([h, total] fp32); returns (out, lse_out)."""
+    n = len(o_parts)
+    if not 1 <= n <= MAX_PARTS or len(lse_parts) != n:
+        raise ValueError("lse_merge_n: 1..8 partials, one lse each")
+    for t in o_parts:
+        _require_cuda("o_part", t, o_parts[0].dtype)
+    for t in lse_parts:
+        _require_cuda("lse_part", t, torch.float32)
+    total, h, d = o_parts[0].shape
+    out = torch.empty_like(o_parts[0]) if out is None else out
+    lse_out = (torch.empty((h, total), dtype=torch.float32, device=out.device)
+               if lse_out is None else lse_out)
+    dt = _lib.THD_BF16 if out.dtype == torch.bfloat16 else _lib.THD_FP16
+    st = _lib_cp().thd_attn_lse_merge_n(_ptr_array(o_parts), _ptr_array(lse_parts), n, _ptr(out),
+                                        _ptr(lse_out), total, h, d, dt, _stream(out.device))
+    _lib.check(st, "thd_attn_lse_merge_n")
+    return out, lse_out
+
+
+def sum_n(parts, *, out=None):
+    """One-pass fp32 sum of up to 8 same-shaped tensors, in their dtype."""
+    n = len(parts)
+    if not 1 <= n <= MAX_PARTS:
+        raise ValueError("sum_n: 1..8 partials")
+    for t in parts:
+        _require_cuda("part", t, parts[0].dtype)
+        if t.numel() != parts[0].numel():
+            raise ValueError("sum_n: sizes differ")
+    out = torch.empty_like(parts[0]) if out is None else out
+    dt = _lib.THD_BF16 if out.dtype == torch.bfloat16 else _lib.THD_FP16
+    st = _lib_cp().thd_sum_n(_ptr_array(parts), n, _ptr(out), out.numel(), dt, _stream(out.device))
+    _lib.check(st, "thd_sum_n")
+    return out
+
+
 def cp_views(cu_seqlens, cp_size, rank, *, mask_type=None, batch_size=None):
     """The (query view, key view) of every ring step of rank ``rank``, in ring
     order (step s reads the keys of rank (rank - s) mod cp_size)."""
@@ -131,12 +181,25 @@ def cp_attn_fwd(q_local, k_shards, v_shards, cu_seqlens, cp_size, rank, max_seql
     b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
     max_local = 2 * ((int(max_seqlen) + 2 * n - 1) // (2 * n))
     T, hq, d = q_local.shape
+    views = views or cp_views(cu_seqlens, n, rank, mask_type=mask_type, batch_size=b)
+    if n <= MAX_PARTS:
+        # every step's output kept, then merged in one pass
+        outs, lses = [], []
+        for t, vq, vk in views:
+            o_s, l_s = attn_fwd(q_local, k_shards[t], v_shards[t], vq["cu_seqlens"],
+                                vk["cu_seqlens"], max_local, max_local,
+                                cu_seqlens_q_padded=vq["cu_seqlens_padded"],
+                                cu_seqlens_kv_padded=vk["cu_seqlens_padded"],
+                                mask_type=vq["mask_type"][:b], softmax_scale=softmax_scale,
+                                batch_size=b)
+            outs.append(o_s)
+            lses.append(l_s)
+        return lse_merge_n(outs, lses)
     o_acc = torch.empty((T, hq, d), dtype=torch.float32, device=q_local.device)
     lse_acc = torch.empty((hq, T), dtype=torch.float32, device=q_local.device)
     out = torch.empty_like(q_local)
     o_step = torch.empty_like(q_local)
     lse_step = torch.empty((hq, T), dtype=torch.float32, device=q_local.device)
-    views = views or cp_views(cu_seqlens, n, rank, mask_type=mask_type, batch_size=b)
     for s, (t, vq, vk) in enumerate(views):
         attn_fwd(q_local, k_shards[t], v_shards[t], vq["cu_seqlens"], vk["cu_seqlens"],
                  max_local, max_local, cu_seqlens_q_padded=vq["cu_seqlens_padded"],
@@ -170,9 +233,8 @@ def cp_attn_bwd(q_local, k_shards, v_shards, out_local, dout_local, lse_local, c
     n = int(cp_size)
     b = cu_seqlens.numel() - 1 if batch_size is None else int(batch_size)
     max_local = 2 * ((int(max_seqlen) + 2 * n - 1) // (2 * n))
-    dq_acc = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
-    dq = torch.empty_like(q_local)
     parts = [None] * n
+    dqs = []
     views = views or cp_views(cu_seqlens, n, rank, mask_type=mask_type, batch_size=b)
     for s, (t, vq, vk) in enumerate(views):
         dq_s, dk_s, dv_s = attn_bwd(
@@ -180,14 +242,22 @@ def cp_attn_bwd(q_local, k_shards, v_shards, out_local, dout_local, lse_local, c
             vq["cu_seqlens"], vk["cu_seqlens"], max_local, max_local,
             cu_seqlens_q_padded=vq["cu_seqlens_padded"], cu_seqlens_kv_padded=vk["cu_seqlens_padded"],
             mask_type=vq["mask_type"][:b], softmax_scale=softmax_scale, batch_size=b)
-        accumulate(dq_s, dq_acc, first=(s == 0), out=dq if s == n - 1 else None)
+        dqs.append(dq_s)
         parts[t] = (dk_s, dv_s)
+    if n <= MAX_PARTS:
+        return sum_n(dqs), parts
+    dq_acc = torch.empty(q_local.shape, dtype=torch.float32, device=q_local.device)
+    dq = torch.empty_like(q_local)
+    for s, dq_s in enumerate(dqs):
+        accumulate(dq_s, dq_acc, first=(s == 0), out=dq if s == n - 1 else None)
     return dq, parts
 
 
 def cp_reduce(parts):
     """Sum of the contributions to one shard (a list of same-shaped tensors) in
     fp32, returned in their dtype."""
+    if len(parts) <= MAX_PARTS:
+        return sum_n(list(parts))
     acc = torch.empty(parts[0].shape, dtype=torch.float32, device=parts[0].device)
     out = torch.empty_like(parts[0])
     for i, p in enumerate(parts):

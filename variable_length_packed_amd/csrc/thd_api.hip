@@ -235,4 +235,54 @@ int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int3
              : THD_ERR_HIP;
 }
 
+int thd_attn_lse_merge_n(const void* const* o_parts, const float* const* lse_parts,
+                         int32_t n_parts, void* o_out, float* lse_out, int64_t total, int32_t h,
+                         int32_t head_dim, int32_t dtype, void* stream) {
+  if (total < 0 || h <= 0 || head_dim <= 0 || head_dim % 8 != 0 || n_parts < 1 ||
+      n_parts > thd::kMaxParts)
+    return THD_ERR_SHAPE;
+  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
+  if (total == 0) return THD_OK;
+  if (!o_parts || !lse_parts || !o_out) return THD_ERR_NULL;
+  thd::MergeNArgs a = {};
+  for (int k = 0; k < n_parts; ++k) {
+    if (!o_parts[k] || !lse_parts[k]) return THD_ERR_NULL;
+    if (!aligned16(o_parts[k])) return THD_ERR_UNSUPPORTED;
+    a.o[k] = o_parts[k];
+    a.lse[k] = lse_parts[k];
+  }
+  if (!aligned16(o_out)) return THD_ERR_UNSUPPORTED;
+  a.n = n_parts;
+  a.o_out = o_out;
+  a.lse_out = lse_out;
+  a.total = total;
+  a.h = h;
+  a.d = head_dim;
+  return thd::launch_lse_merge_n(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
+             ? THD_OK
+             : THD_ERR_HIP;
+}
+
+int thd_sum_n(const void* const* parts, int32_t n_parts, void* out, int64_t n_elems,
+              int32_t dtype, void* stream) {
+  if (n_elems < 0 || n_elems % 8 != 0 || n_parts < 1 || n_parts > thd::kMaxParts)
+    return THD_ERR_SHAPE;
+  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
+  if (n_elems == 0) return THD_OK;
+  if (!parts || !out) return THD_ERR_NULL;
+  thd::SumNArgs a = {};
+  for (int k = 0; k < n_parts; ++k) {
+    if (!parts[k]) return THD_ERR_NULL;
+    if (!aligned16(parts[k])) return THD_ERR_UNSUPPORTED;
+    a.x[k] = parts[k];
+  }
+  if (!aligned16(out)) return THD_ERR_UNSUPPORTED;
+  a.n = n_parts;
+  a.out = out;
+  a.count = n_elems;
+  return thd::launch_sum_n(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
+             ? THD_OK
+             : THD_ERR_HIP;
+}
+
 }  // extern "C"

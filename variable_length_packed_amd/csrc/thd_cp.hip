@@ -242,7 +242,100 @@ __global__ __launch_bounds__(256) void thd_accumulate_kernel(AccumulateArgs a) {
   }
 }
 
+// (row, head) pairs, d / 8 lanes each: the log-sum-exp merge of n partials
+// in one pass.  With m = max_k lse_k and w_k = exp(lse_k - m):
+// lse = m + log(sum_k w_k), o = sum_k (w_k / sum_j w_j) o_k, in fp32; a pair
+// whose partials are all -inf gets lse -inf and o = 0.
+template <class DT>
+__global__ __launch_bounds__(256) void thd_lse_merge_n_kernel(MergeNArgs a) {
+  const int kch = a.d / 8;
+  const int64_t pairs = a.total * a.h;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t pr = i / kch;
+  const int c = (int)(i - pr * kch);
+  if (pr >= pairs) return;
+  const int64_t row = pr / a.h;
+  const int hh = (int)(pr - row * a.h);
+  const int64_t li = (int64_t)hh * a.total + row;
+  float l[kMaxParts];
+  float m = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k) {
+    l[k] = k < a.n ? a.lse[k][li] : -INFINITY;
+    m = fmaxf(m, l[k]);
+  }
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float lse = -INFINITY;
+  if (m != -INFINITY) {
+    float wsum = 0.f;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) {
+      l[k] = l[k] == -INFINITY ? 0.f : expf(l[k] - m);  // weight (0 for k >= n)
+      wsum += l[k];
+    }
+    lse = m + logf(wsum);
+    const float inv = 1.f / wsum;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) {
+      if (k >= a.n || l[k] == 0.f) continue;
+      const float wk = l[k] * inv;
+      const u32x4 pv = *(const u32x4*)((const uint16_t*)a.o[k] + pr * a.d + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        o[e] += wk * DT::to_f32((uint16_t)(pv[e >> 1] >> (16 * (e & 1))));
+    }
+  }
+  u32x4 out;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    out[k] = (uint32_t)DT::bits(o[2 * k]) | ((uint32_t)DT::bits(o[2 * k + 1]) << 16);
+  *(u32x4*)((uint16_t*)a.o_out + pr * a.d + 8 * c) = out;
+  if (a.lse_out && c == 0) a.lse_out[li] = lse;
+}
+
+// Sum of n partials, 8 elements per thread, in fp32 (partials added in
+// order), written once in the storage dtype.
+template <class DT>
+__global__ __launch_bounds__(256) void thd_sum_n_kernel(SumNArgs a) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= a.count) return;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kMaxParts; ++k) {
+    if (k >= a.n) break;
+    const u32x4 v = *(const u32x4*)((const uint16_t*)a.x[k] + i);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] += DT::to_f32((uint16_t)(v[e >> 1] >> (16 * (e & 1))));
+  }
+  u32x4 w;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    w[k] = (uint32_t)DT::bits(o[2 * k]) | ((uint32_t)DT::bits(o[2 * k + 1]) << 16);
+  *(u32x4*)((uint16_t*)a.out + i) = w;
+}
+
 }  // namespace
+
+hipError_t launch_lse_merge_n(const MergeNArgs& a, bool bf16, hipStream_t s) {
+  const int64_t work = a.total * a.h * (a.d / 8);
+  if (work == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((work + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(thd_lse_merge_n_kernel<Bf16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(thd_lse_merge_n_kernel<Fp16>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_n(const SumNArgs& a, bool bf16, hipStream_t s) {
+  if (a.count == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((a.count / 8 + 255) / 256);
+  if (bf16)
+    hipLaunchKernelGGL(thd_sum_n_kernel<Bf16>, dim3(blocks), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL(thd_sum_n_kernel<Fp16>, dim3(blocks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_accumulate(const AccumulateArgs& a, bool bf16, hipStream_t s) {
   if (a.n == 0) return hipSuccess;

@@ -93,6 +93,26 @@ struct AccumulateArgs {
 };
 
 hipError_t launch_accumulate(const AccumulateArgs& a, bool bf16, hipStream_t s);
+
+// One pass over up to kMaxParts partials: their log-sum-exp merge, or their sum.
+constexpr int kMaxParts = 8;
+struct MergeNArgs {
+  const void* o[kMaxParts];      // [total, h, d] storage dtype
+  const float* lse[kMaxParts];   // [h, total]
+  int n;
+  void* o_out;                   // [total, h, d] storage dtype
+  float* lse_out;                // [h, total]; may be null
+  int64_t total;
+  int h, d;
+};
+struct SumNArgs {
+  const void* x[kMaxParts];  // count elements, storage dtype
+  int n;
+  void* out;                 // count elements, storage dtype
+  int64_t count;             // multiple of 8
+};
+hipError_t launch_lse_merge_n(const MergeNArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_sum_n(const SumNArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_cp_layout(const CpLayoutArgs& a, hipStream_t s);
 hipError_t launch_cp_gather(const CpGatherArgs& a, hipStream_t s);
 hipError_t launch_lse_merge(const MergeArgs& a, bool bf16, hipStream_t s);
