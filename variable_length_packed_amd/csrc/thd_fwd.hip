@@ -28,7 +28,15 @@ namespace thd {
 namespace {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup
-constexpr int kFwdBN = 64;   // keys per LDS tile
+// Keys per LDS tile and tiles in flight.  At d > 32 the tiles hold 32 keys in
+// three stages (48 KB per workgroup at d = 128), so that three workgroups, or
+// three waves per SIMD, share a CU; at d <= 32 a 32-key tile would be smaller
+// than one 1 KB load per wave, and 64-key tiles in two stages are kept.
+template <int DP>
+struct FwdTile {
+  static constexpr int BN = DP > 32 ? 32 : 64;
+  static constexpr int NS = DP > 32 ? 3 : 2;
+};
 constexpr int kWaveM = 32;   // query rows per wave
 constexpr int kZeroRows = 64;
 
@@ -55,12 +63,12 @@ struct FwdParams {
 // Schedule of the attention workgroups (largest first, see build_schedule):
 // query tile t of sequence b walks W = ceil(lk / BN) key tiles, or, with a
 // causal mask type, the tiles up to its last row's diagonal:
-// W = ceil(clamp(min(lk, (t + 1) BM + off), 0) / BN) = clamp(2t + 2 + ceil(off / BN), 0, ceil(lk / BN))
-// (BM = 2 BN), with the kernel's clamping of the lengths.
-static_assert(kFwdBM == 2 * kFwdBN, "work model assumes two key tiles per query tile");
-
+// W = ceil(clamp(min(lk, (t + 1) BM + off), 0) / BN) = clamp(a t + a + ceil(off / BN), 0, ceil(lk / BN))
+// with a = BM / BN, and the kernel's clamping of the lengths.
+template <int BN>
 struct FwdSchedModel {
-  static constexpr int kSlope = 2;
+  static_assert(kFwdBM % BN == 0, "work model assumes whole key tiles per query tile");
+  static constexpr int kSlope = kFwdBM / BN;
   const FwdParams& p;
   __device__ SeqSummary seq(int b) const {
     const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
@@ -72,9 +80,9 @@ struct FwdSchedModel {
     const int mt = mask_type_of(p.causal, b);
     SeqSummary s;
     s.x = ceil_div_pos(lq, kFwdBM);
-    s.H = ceil_div_pos(lk, kFwdBN);
+    s.H = ceil_div_pos(lk, BN);
     s.causal = mask_is_causal(mt);
-    s.c = 2 + ceil_div(causal_offset(mt, lq, lk), kFwdBN);
+    s.c = kSlope + ceil_div(causal_offset(mt, lq, lk), BN);
     return s;
   }
 };
@@ -107,10 +115,12 @@ __device__ void fwd_zero_pad_rows(const FwdParams& p, int zb) {
   }
 }
 
-// pre: schedule of the attention workgroups, then zeros on pad rows.
+// pre: schedule of the attention workgroups (key tiles of BN keys), then
+// zeros on pad rows.
+template <int BN>
 __global__ __launch_bounds__(256) void thd_fwd_pre_kernel(FwdParams p) {
   if ((int)blockIdx.x < p.n_sched) {
-    build_schedule(FwdSchedModel{p}, p.batch, p.n_tiles, p.sched,
+    build_schedule(FwdSchedModel<BN>{p}, p.batch, p.n_tiles, p.sched,
                    blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
@@ -123,16 +133,19 @@ __global__ __launch_bounds__(256) void thd_fwd_pre_kernel(FwdParams p) {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <class DT, int DP>
-__global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
-  constexpr int BM = kFwdBM, BN = kFwdBN;
+__global__ __launch_bounds__(256, DP > 32 ? 3 : 2) void thd_fwd_kernel(FwdParams p) {
+  constexpr int BM = kFwdBM, BN = FwdTile<DP>::BN, NS = FwdTile<DP>::NS;
+  constexpr int NT = BN / 32;      // 32-key S^T tiles per LDS tile
+  constexpr int NKB = BN / 16;     // 16-key blocks (MFMA K steps of O^T)
   constexpr int NC = DP / 16;      // 16-wide d blocks (MFMA K steps of S^T)
   constexpr int ND = DP / 32;      // 32-row d tiles of O^T
   constexpr int KCH = DP / 8;      // 16-byte chunks per K row
   constexpr int TILE = BN * DP * 2;  // bytes of one K or V tile
   constexpr int BPW = TILE / 1024 / 4;  // 1 KB blocks (one load each) per wave per tile
   static_assert(BPW >= 1 && BPW * 4096 == TILE, "tile splits into 1 KB blocks over 4 waves");
+  static_assert(2 * BPW < 16, "loads of one tile fit the vmcnt field");
   // buffer j: K tile at 2j * TILE, V tile at (2j + 1) * TILE
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[4 * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TILE];
 
   // Workgroups in schedule order (largest items first), query heads minor:
   // with h_q a multiple of 8, head hq always lands on XCD hq % 8, whose L2
@@ -229,19 +242,23 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
   const uint32_t b_t = swz<DP>(4 * h + (g16 >> 2), 16 * (grp & 1) + 4 * (g16 & 3));
 
   const float c2 = p.c2;
-  if (n_kv_tiles > 0) load_tile(0, 0);
-  // vmcnt(0): the first tile and the Q operand are in.  Saying so also keeps
-  // the compiler from treating the Q loads as pending at the loop head, where
-  // it would otherwise wait, inside the S products, for the next tile.
+  // Tiles 0 .. NS-2 go in flight before the loop; iteration it issues tile
+  // it + NS - 1 into the buffer that iteration it - 1 read.
+#pragma unroll
+  for (int t = 0; t < NS - 1; ++t)
+    if (t < n_kv_tiles) load_tile(t * BN, t);
+  // vmcnt(0): the Q operand and the first tiles are in.  The full wait (once
+  // per workgroup) also tells the compiler, which does not count the tile
+  // loads, that the Q loads are done; otherwise it would treat them as
+  // pending at the loop head and wait, inside the S products, for every load.
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
+  int buf = 0, lbuf = NS - 1;  // buffer read by this iteration, buffer it loads
   for (int it = 0; it < n_kv_tiles; ++it) {
     const int k0 = it * BN;
-    const int buf = it & 1;
-    const bool more = it + 1 < n_kv_tiles;
-    // The other buffer was last read in the previous iteration, which every
-    // wave has left (barrier below).
-    if (more) load_tile(k0 + BN, buf ^ 1);
+    // The buffer loaded here was last read in the previous iteration, which
+    // every wave has left (barrier below).
+    if (it + NS - 1 < n_kv_tiles) load_tile(k0 + (NS - 1) * BN, lbuf);
 
     const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + kWaveM - 1 + off);
     if (active) {
@@ -250,9 +267,9 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
       const uint32_t bo = (uint32_t)(2 * buf * TILE);
       const uint32_t a_k = opaque(b_k + bo), a_t = opaque(b_t + bo);
       // S^T tiles: rows = keys k0 + 32*tt + (C row), columns = this wave's queries
-      f32x16 s[2];
+      f32x16 s[NT];
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt) {
+      for (int tt = 0; tt < NT; ++tt) {
         s[tt] = f32x16{};
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
@@ -266,7 +283,7 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
         // keys j < lim visible (lim <= 0: none)
         const int lim = causal ? (my_q + 1 + off < lk ? my_q + 1 + off : lk) : lk;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+        for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
             const int j = k0 + 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
@@ -276,7 +293,7 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
 
       float mt = -__builtin_inff();
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
       mt = fmaxf(mt, wave_swap_halves(mt));
@@ -295,7 +312,7 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
       }
       const float mc = m_run == -__builtin_inff() ? 0.f : m_run * c2;
 #pragma unroll
-      for (int tt = 0; tt < 2; ++tt)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, -mc));
@@ -303,9 +320,9 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
           l_run += e;
         }
 
-      typename DT::vec8 pb[4];
+      typename DT::vec8 pb[NKB];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
+      for (int kb = 0; kb < NKB; ++kb) {
         float tmp[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) tmp[j] = s[kb >> 1][8 * (kb & 1) + j];
@@ -314,15 +331,22 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
           const u32x4 a =
               cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + TILE + tr_row<DP>(kb, 0)),
                    lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + TILE + tr_row<DP>(kb, 1)));
           acc[dt] = DT::mfma(as_vec8<DT>(a), pb[kb], acc[dt]);
         }
     }
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's part of the next tile is in LDS
+    // This wave's part of tile it + 1 is in LDS: the loads of later tiles
+    // (NS - 2 of them at most, 2 BPW loads each) may still be pending.
+    if (NS > 2 && it + 2 < n_kv_tiles)
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (NS > 2 ? 2 * BPW : 0));
+    else
+      __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
+    buf = buf + 1 == NS ? 0 : buf + 1;
+    lbuf = lbuf + 1 == NS ? 0 : lbuf + 1;
   }
 
   // Epilogue: O = acc / l, LSE = m * scale + ln(l).  Rows past lq are dropped
@@ -349,8 +373,16 @@ __global__ __launch_bounds__(256, 2) void thd_fwd_kernel(FwdParams p) {
         lt > 0.f ? m_run * p.scale + __logf(lt) : -__builtin_inff();
 }
 
+// Pre pass (schedule for this head dim's key tiles, pad rows), then attention.
 template <class DT, int DP>
-hipError_t launch_fwd_t(const FwdParams& fp, hipStream_t s) {
+hipError_t launch_fwd_t(const FwdParams& fp, int64_t n_pre, hipStream_t s) {
+  if (n_pre > 0) {
+    hipLaunchKernelGGL((thd_fwd_pre_kernel<FwdTile<DP>::BN>), dim3((unsigned)n_pre), dim3(256), 0,
+                       s, fp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (fp.n_attn == 0) return hipSuccess;
   hipLaunchKernelGGL((thd_fwd_kernel<DT, DP>), dim3(fp.n_attn), dim3(256), 0, s, fp);
   return hipGetLastError();
 }
@@ -383,7 +415,8 @@ static FwdParams pad_params(const Problem& p, void* o, float* lse) {
 hipError_t launch_fwd_pad_rows(const Problem& p, void* o, float* lse, hipStream_t s) {
   const int64_t n_zero = (p.T_q + kZeroRows - 1) / kZeroRows;
   if (n_zero == 0) return hipSuccess;
-  hipLaunchKernelGGL(thd_fwd_pre_kernel, dim3((unsigned)n_zero), dim3(256), 0, s,
+  // no schedule (n_sched = 0): any key tile size
+  hipLaunchKernelGGL(thd_fwd_pre_kernel<FwdTile<128>::BN>, dim3((unsigned)n_zero), dim3(256), 0, s,
                      pad_params(p, o, lse));
   return hipGetLastError();
 }
@@ -418,15 +451,11 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
   fp.sched = (int32_t*)workspace;
   const int64_t n_zero = (p.T_q + kZeroRows - 1) / kZeroRows;
   const int64_t n_pre = fp.n_sched + n_zero;
-  if (n_pre > 0) {
-    hipLaunchKernelGGL(thd_fwd_pre_kernel, dim3((unsigned)n_pre), dim3(256), 0, s, fp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  if (fp.n_attn == 0) return hipSuccess;
-  if (p.d <= 32) return p.bf16 ? launch_fwd_t<Bf16, 32>(fp, s) : launch_fwd_t<Fp16, 32>(fp, s);
-  if (p.d <= 64) return p.bf16 ? launch_fwd_t<Bf16, 64>(fp, s) : launch_fwd_t<Fp16, 64>(fp, s);
-  return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, s) : launch_fwd_t<Fp16, 128>(fp, s);
+  if (p.d <= 32)
+    return p.bf16 ? launch_fwd_t<Bf16, 32>(fp, n_pre, s) : launch_fwd_t<Fp16, 32>(fp, n_pre, s);
+  if (p.d <= 64)
+    return p.bf16 ? launch_fwd_t<Bf16, 64>(fp, n_pre, s) : launch_fwd_t<Fp16, 64>(fp, n_pre, s);
+  return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, n_pre, s) : launch_fwd_t<Fp16, 128>(fp, n_pre, s);
 }
 
 }  // namespace thd
