@@ -54,30 +54,59 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest():
-    """Digest of the HIP sources; counter-based traffic is valid only for them."""
-    import glob
+# Sources each timed kernel is built from: a counter record of a kernel stays
+# valid while these files are unchanged.
+KERNEL_SOURCES = {
+    "thd_bwd_main_kernel": ("thd_bwd.hip", "thd_common.hpp", "thd_launch.hpp"),
+    "thd_fwd_kernel": ("thd_fwd.hip", "thd_common.hpp", "thd_launch.hpp"),
+}
+
+
+def source_digest(kernel):
+    """Digest of the HIP sources of one kernel; its counter-based traffic is
+    valid only for them."""
     import hashlib
     h = hashlib.sha256()
-    for path in sorted(glob.glob(os.path.join(ROOT, "variable_length_packed_amd", "csrc", "*"))):
-        h.update(os.path.basename(path).encode())
-        with open(path, "rb") as f:
+    for name in KERNEL_SOURCES[kernel]:
+        h.update(name.encode())
+        with open(os.path.join(ROOT, "variable_length_packed_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel, workload_tag):
-    """HBM bytes per launch from the committed FETCH_SIZE / WRITE_SIZE record
-    of this kernel and workload, or None when the kernel has changed since."""
+def counter_record(kernel, workload_tag):
+    """The committed rocprofv3 counter record of this kernel and workload, or
+    None when the kernel has changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload_tag}_traffic.json")
     try:
         with open(path) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("source_digest") != source_digest():
+    if kernel not in KERNEL_SOURCES or rec.get("source_digest") != source_digest(kernel):
         return None
-    return int(rec["bytes_per_launch"])
+    return rec
+
+
+def measured_traffic(kernel, workload_tag):
+    """HBM bytes per launch (FETCH_SIZE / WRITE_SIZE, copy-calibrated)."""
+    rec = counter_record(kernel, workload_tag)
+    return None if rec is None else int(rec["bytes_per_launch"])
+
+
+def measured_busy(workload_tag):
+    """MFMA-busy and LDS-active percentages of the attention kernels, from the
+    committed counter records (SQ_VALU_MFMA_BUSY_CYCLES / SIMDs, and
+    SQ_LDS_IDX_ACTIVE / CUs, over GRBM_GUI_ACTIVE), and the HBM rate those
+    records' traffic gives at this run's kernel times."""
+    out = {}
+    for kernel in KERNEL_SOURCES:
+        rec = counter_record(kernel, workload_tag)
+        if rec is not None and "mfma_busy_pct" in rec:
+            out[kernel] = {"mfma_busy_pct": rec["mfma_busy_pct"],
+                           "lds_active_pct": rec["lds_active_pct"],
+                           "hbm_bytes_per_launch": rec["bytes_per_launch"]}
+    return out or None
 
 
 def copy_calibration(mib):
@@ -293,6 +322,10 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (measured_traffic(dom, "16seq_causal_h16_d128") if w.name == "2" else None),
                 "avg_launch_ms": round(dom_ms, 4)}
+    busy = measured_busy("16seq_causal_h16_d128") if w.name == "2" else None
+    if busy is not None:
+        for kernel, rec in busy.items():
+            rec["hbm_gbs"] = round(rec["hbm_bytes_per_launch"] / (kern[kernel][0] * 1e-3) / 1e9, 1)
 
     out = {
         "metric": "packed-THD attention valid-pair TFLOP/s fwd+bwd; % of MI355X bf16 MFMA peak",
@@ -312,6 +345,8 @@ def main():
         "value_no_recompute_credit": round(value * 12 / 14, 2),
         "step_ms_events": {"median": round(step_ms[len(step_ms) // 2], 4),
                            "min": round(step_ms[0], 4)},
+        # rocprofv3 counters of the attention kernels on this workload and build
+        "counters": busy,
         # the same step replayed from one HIP graph (no launch gaps)
         "graph_replay": None if graph_ms is None else {
             "ms_per_step": round(graph_ms, 4),
