@@ -78,9 +78,29 @@ __device__ __forceinline__ typename DT::vec8 pack8(const float* x) {
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-__device__ __forceinline__ float wave_swap_halves(float x) {
-  // value held by lane l ^ 32
-  return __shfl_xor(x, 32, 64);
+// Max and sum of x over lanes l and l ^ 32, in every lane.  v_permlane32_swap
+// exchanges lanes 32-63 of its first register with lanes 0-31 of its second,
+// so with x in both, each lane ends up holding its own value in one register
+// and its partner's in the other: a symmetric combination of the two needs no
+// lane select, and no LDS round trip as a bpermute would.  Written as
+// assembly with both registers as in/out operands (the compiler builtin,
+// given the same value twice, was folded as if the swap were a no-op); the
+// s_nop covers the wait states between the VALU writes of the copies and the
+// permlane's reads.  Every lane of the wave must be active.
+__device__ __forceinline__ void halves_pair(float x, float& a, float& b) {
+  a = x;
+  b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float wave_max_halves(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float wave_sum_halves(float x) {
+  float a, b;
+  halves_pair(x, a, b);
+  return a + b;
 }
 
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }

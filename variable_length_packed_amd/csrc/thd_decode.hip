@@ -153,7 +153,7 @@ __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
     float mt = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[i]);
-    mt = fmaxf(mt, wave_swap_halves(mt));
+    mt = wave_max_halves(mt);
     const float m_new = fmaxf(m_run, mt);
     if (m_new != -__builtin_inff() && m_new != m_run) {
       const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((m_run - m_new) * c2);
@@ -203,8 +203,8 @@ __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
   }
 
   // Partial of this chunk for query row r: acc holds O^T[32dt + 8g + 4h + e][r].
+  const float lt = wave_sum_halves(l_run);  // every lane still active here
   if (!row_ok) return;
-  const float lt = l_run + wave_swap_halves(l_run);
   const int64_t idx = (((int64_t)b * p.h_q + hq) * p.lq_max + qi) * p.n_split + split;
   float* po = p.part_o + idx * DP;
 #pragma unroll

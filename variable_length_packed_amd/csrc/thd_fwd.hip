@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, DP > 32 ? 3 : 2) void thd_fwd_kernel(FwdParams
       for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mt = fmaxf(mt, s[tt][i]);
-      mt = fmaxf(mt, wave_swap_halves(mt));
+      mt = wave_max_halves(mt);
       // Move the running max only when it grew by more than 2^8 in exp2 units.
       const bool grow = mt != -__builtin_inff() &&
                         (m_run == -__builtin_inff() || (mt - m_run) * c2 > kRescaleLog2);
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(256, DP > 32 ? 3 : 2) void thd_fwd_kernel(FwdParams
 
   // Epilogue: O = acc / l, LSE = m * scale + ln(l).  Rows past lq are dropped
   // by the resource bound.
-  const float lt = l_run + wave_swap_halves(l_run);
+  const float lt = wave_sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
   const uint32_t orow = (uint32_t)my_q * qrow_bytes;
 #pragma unroll
