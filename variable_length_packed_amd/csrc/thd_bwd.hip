@@ -116,17 +116,22 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   // -LSE/scale only at rows inside a sequence (through range-limited
   // resources), and the accumulator of a pad row receives no atomics, so it
   // stays zero and converts to the +0 the pad rows of dq need.
-  int64_t pr[2];
+  int64_t pr[2], si[2];
   u32x4 a[2], gr[2];
+  float lse_v[2] = {0.f, 0.f};
+  // All loads first (the LSE too), so that each wave has them in flight at once.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
     pr[t] = p0 + g + t * (PB / 2);
+    const int64_t row = pr[t] / p.h_q;
+    si[t] = (pr[t] - row * p.h_q) * p.T_q + row;  // statistics: [h_q][T_q]
     a[t] = gr[t] = u32x4{0u, 0u, 0u, 0u};
     if (pr[t] < pairs && 8 * c < p.d) {
       const int64_t off = pr[t] * p.d + 8 * c;  // o, dout: [T_q][h_q][d]
       a[t] = *(const u32x4*)(p.o + off);
       gr[t] = *(const u32x4*)(p.dout + off);
     }
+    if (pr[t] < pairs && c == 1) lse_v[t] = p.lse[si[t]];
   }
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
@@ -136,19 +141,19 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
       *(f32x4*)dst = z;
       *(f32x4*)(dst + 4) = z;
     }
+  }
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
     float acc = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
       acc += DT::to_f32((uint16_t)(a[t][w] & 0xffffu)) * DT::to_f32((uint16_t)(gr[t][w] & 0xffffu));
       acc += DT::to_f32((uint16_t)(a[t][w] >> 16)) * DT::to_f32((uint16_t)(gr[t][w] >> 16));
     }
-#pragma unroll
-    for (int m = KCH / 2; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, KCH);
+    acc = group_sum<KCH>(acc);
     if (pr[t] < pairs && c < 2) {
-      const int64_t row = pr[t] / p.h_q;
-      const int64_t i = (pr[t] - row * p.h_q) * p.T_q + row;  // statistics: [h_q][T_q]
-      if (c == 0) p.dsum[i] = -acc;                           // -D
-      else p.lsum[i] = p.lse[i] * (-1.0f / p.scale);          // -LSE / scale
+      if (c == 0) p.dsum[si[t]] = -acc;                     // -D
+      else p.lsum[si[t]] = lse_v[t] * (-1.0f / p.scale);   // -LSE / scale
     }
   }
 }
