@@ -590,418 +590,6 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// main, one wave per SIMD (d = 128): the workgroup of the kernel above with
-// 4 waves of 64 keys each instead of 8 of 32.  A wave keeps dK^T / dV^T of its
-// two 32-key halves (256 accumulators, in AGPRs), so every Q and dO operand it
-// reads from LDS feeds two products, and dQ is formed by 32x32x16 products
-// (wave w takes d columns 32w .. 32w+31 over all 256 keys).  LDS as above.
-// dS is stored with each 16-key block's groups of four keys in the order
-// 0, 2, 1, 3, so that the 8 keys one lane half supplies to a dQ product
-// (keys 4h .. 4h+3 and 8+4h .. 8+4h+3 of the block, the order in which the
-// K^T transpose reads deliver them) are 16 contiguous bytes.
-// ---------------------------------------------------------------------------
-// dK^T / dV^T products with the accumulator held in AGPRs.  Written as
-// assembly with an AGPR operand so that the 256 accumulators of a wave stay in
-// the AGPR file (the builtin leaves their placement to the register
-// allocator, which moved them back and forth).  The compiler does not see the
-// product inside the assembly, so the wait states it would insert are
-// explicit: WAIT_VALU covers a VALU write of an operand just before (the
-// packed P and dS); accumulation chains on the same registers need none.
-template <class DT, bool WAIT_VALU>
-__device__ __forceinline__ void mfma_agpr(f32x16& acc, typename DT::vec8 a, typename DT::vec8 b) {
-  if constexpr (std::is_same<DT, Bf16>::value) {
-    if constexpr (WAIT_VALU)
-      asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  } else {
-    if constexpr (WAIT_VALU)
-      asm volatile("s_nop 4\n\tv_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-    else
-      asm volatile("v_mfma_f32_32x32x16_f16 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-  }
-}
-
-__device__ __forceinline__ int ds_pos(int key) {
-  const int o = key & 15, g = o >> 2;
-  return (key & ~15) | ((((g & 1) << 1) | (g >> 1)) << 2) | (o & 3);
-}
-
-template <class DT>
-__global__ __launch_bounds__(256, 1) void thd_bwd_main4_kernel(BwdParams p) {
-  constexpr int DP = 128;
-  constexpr int BK = kBwdBK, BQ = kBwdBQ;
-  constexpr int NC = DP / 16;
-  constexpr int ND = DP / 32;
-  constexpr int KCH = DP / 8;
-  constexpr int TILE = BQ * DP * 2;
-  constexpr int OFF_DS = 0;
-  constexpr int OFF_Q = OFF_DS + BQ * BK * 2;
-  constexpr int OFF_DO = OFF_Q + TILE;
-  constexpr int OFF_K = OFF_DO + TILE;
-  constexpr int OFF_V = OFF_K + BK * DP * 2;
-  constexpr int SMEM = OFF_V + BK * DP * 2;
-  static_assert(SMEM <= 163840, "LDS budget of one workgroup");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  unsigned char* Kt = smem + OFF_K;
-  unsigned char* Vt = smem + OFF_V;
-  unsigned char* Qb = smem + OFF_Q;
-  unsigned char* Ob = smem + OFF_DO;
-  unsigned char* dSs = smem + OFF_DS;
-
-  const int bid = blockIdx.x;
-  const int rk = bid / p.h_kv;
-  const int hk = bid - rk * p.h_kv;
-  if (rk >= p.sched[0]) return;
-  const int b = uniform(p.sched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
-  if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
-
-  const int tid = threadIdx.x;
-  const int w = uniform(tid >> 6);  // keys 64w .. 64w+63; dQ columns 32w .. 32w+31
-  const int l = tid & 63;
-  const int r = l & 31;
-  const int h = l >> 5;
-  const int g16 = l & 15;
-  const int grp = l >> 4;
-
-  const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
-  const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const uint32_t accrow_bytes = (uint32_t)p.h_q * DP * 4;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
-  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const int mtype = mask_type_of(p.causal, b);
-  const bool causal = mask_is_causal(mtype);
-  const int off = causal_offset(mtype, lq, lk);  // key j visible to query i iff j <= i + off
-  const int k0 = tile_in_seq * BK;
-  if (k0 >= lk) return;
-  const int kw0 = k0 + 64 * w;
-
-  // Keys [k0, lk) of kv head hk -> LDS; rows past lk read as zeros.
-  const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
-  const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
-  const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
-  {
-    const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
-    const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
-#pragma unroll
-    for (int i = 0; i < BK * KCH / 256; ++i) {
-      const int cid = tid + 256 * i;
-      const int row = cid / KCH;
-      const int x = cid - row * KCH;
-      const uint32_t o = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
-      *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, o, 0);
-      *(u32x4*)(Vt + swz<DP>(row, 8 * x)) = buf_load16(v_rs, o, 0);
-    }
-  }
-
-  const int q_start = causal ? max(floor_div(k0 - off, BQ), 0) * BQ : 0;
-  const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
-  const int n_iter = p.group * n_qt;
-
-  // Staging of the next query tile: BQ * KCH chunks each of Q and dO, two per thread.
-  uint32_t s_off[2], s_lds[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cid = tid + 256 * j;
-    const int row = cid / KCH;
-    const int x = cid - row * KCH;
-    s_off[j] = 8 * x < p.d ? (uint32_t)row * qrow_bytes + 16u * x : kOobOffset;
-    s_lds[j] = swz<DP>(row, 8 * x);
-  }
-  u32x4 qreg[2], oreg[2];
-  auto load_q = [&](int hq_, int q0_, bool real) {
-    const int64_t hoff = sq * (int64_t)p.h_q * p.d + (int64_t)hq_ * p.d;
-    const rsrc_t q_rs = make_rsrc(p.q + hoff, (uint32_t)lq * qrow_bytes);
-    const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t o =
-          (s_off[j] == kOobOffset || !real) ? kOobOffset : s_off[j] + (uint32_t)q0_ * qrow_bytes;
-      qreg[j] = buf_load16(q_rs, o, 0);
-      oreg[j] = buf_load16(o_rs, o, 0);
-    }
-  };
-  auto store_q = [&]() {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      *(u32x4*)(Qb + s_lds[j]) = qreg[j];
-      *(u32x4*)(Ob + s_lds[j]) = oreg[j];
-    }
-  };
-
-  f32x16 dk_acc[2][ND], dv_acc[2][ND];
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh)
-#pragma unroll
-    for (int i = 0; i < ND; ++i) {
-      dk_acc[kh][i] = f32x16{};
-      dv_acc[kh][i] = f32x16{};
-    }
-
-  const int tr_row_l = g16 >> 2;
-  const int tr_col = 4 * (g16 & 3);
-  const float c2 = p.c2;
-  const uint32_t b_q = swz<DP>(r, 8 * h);
-  const uint32_t b_t = swz<DP>(4 * h + tr_row_l, 16 * (grp & 1) + tr_col);
-
-  int hq = hk * p.group, q0 = q_start;
-  auto advance = [&](int& hq_, int& q0_) {
-    q0_ += BQ;
-    if (q0_ >= lq) {
-      q0_ = q_start;
-      ++hq_;
-    }
-  };
-  // dQ of a query tile, added to the accumulator right after its products.
-  f32x16 dq = f32x16{};
-  int hq_p = hq, q0_p = q0;
-  const int dcol = 32 * w + r;
-  rsrc_t acc_rs;
-  uint32_t acc_base = kOobOffset;
-  auto setup_dq = [&](bool real) {
-    acc_rs = make_rsrc(p.dq_acc + (sq * p.h_q + hq_p) * DP, (uint32_t)lq * accrow_bytes);
-    acc_base = (real && dcol < p.d) ? (uint32_t)(q0_p + 4 * h) * accrow_bytes + dcol * 4u
-                                    : kOobOffset;
-  };
-  // atomic j (0..15): register j, row q0_p + 8(j / 4) + 4h + j % 4
-  auto atomic_dq = [&](int j) {
-    buf_atomic_add(dq[j], acc_rs,
-                   acc_base == kOobOffset
-                       ? kOobOffset
-                       : acc_base + (uint32_t)(8 * (j >> 2) + (j & 3)) * accrow_bytes,
-                   0);
-  };
-
-  f32x16 s[2], dp[2];
-  rsrc_t l_rs, d_rs;
-  uint32_t st_off = kOobOffset;
-  auto setup_stats = [&](int hq_, int q0_, bool real) {
-    const int64_t roff = real ? (int64_t)hq_ * p.T_q + sq : 0;
-    l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
-    d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
-    st_off = real ? (uint32_t)(q0_ + 4 * h) * 4u : kOobOffset;
-  };
-  auto load_stat = [&](int j) {
-    const int m = j >> 1;
-    const uint32_t o = st_off == kOobOffset ? kOobOffset : st_off + 32u * m;
-    const f32x4 v = __builtin_bit_cast(f32x4, buf_load16((j & 1) ? d_rs : l_rs, o, 0));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (j & 1)
-        dp[0][4 * m + e] = v[e];
-      else
-        s[0][4 * m + e] = v[e];
-    }
-  };
-
-  if (n_iter > 0) {
-    setup_stats(hq, q0, true);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) load_stat(j);
-    load_q(hq, q0, true);
-    store_q();
-  }
-  __syncthreads();  // K, V and the first query tile visible
-  for (int iter = 0; iter < n_iter; ++iter) {
-    const bool more = iter + 1 < n_iter;
-    int hq_n = hq, q0_n = q0;
-    advance(hq_n, q0_n);
-
-    load_q(hq_n, q0_n, more);
-    setup_stats(hq_n, q0_n, more);
-    s[1] = s[0];
-    dp[1] = dp[0];
-
-    {
-      // S = Q K^T and dP = dO V^T for both key halves; one Q and one dO
-      // operand per step feed both.
-      u32x4 qa[2], oa[2], ka[2][2], va[2][2];
-      auto ld_s = [&](int c, int slot) {
-        const uint32_t cx = (uint32_t)c << 5;
-        qa[slot] = *(const u32x4*)(Qb + (b_q ^ cx));
-        oa[slot] = *(const u32x4*)(Ob + (b_q ^ cx));
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          const uint32_t kr = (uint32_t)(64 * w + 32 * kh) * (DP * 2);
-          ka[kh][slot] = *(const u32x4*)(Kt + kr + (b_q ^ cx));
-          va[kh][slot] = *(const u32x4*)(Vt + kr + (b_q ^ cx));
-        }
-      };
-      ld_s(0, 0);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) ld_s(c + 1, (c + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int kh = 0; kh < 2; ++kh) {
-          s[kh] = DT::mfma(as_vec8<DT>(qa[c & 1]), as_vec8<DT>(ka[kh][c & 1]), s[kh]);
-          dp[kh] = DT::mfma(as_vec8<DT>(oa[c & 1]), as_vec8<DT>(va[kh][c & 1]), dp[kh]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    typename DT::vec8 pb[2][2], db[2][2];
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int kwk = kw0 + 32 * kh;
-      const int my_k = kwk + r;
-      const bool need_mask =
-          (kwk + 32 > lk) || (q0 + BQ > lq) || (causal && kwk + 31 > q0 + off);
-      if (__builtin_expect(need_mask, 0)) {
-        const int lim_lo = causal ? my_k - q0 - off : -1;
-        const int row_hi = my_k < lk ? lq - q0 : 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!(qi >= lim_lo && qi < row_hi)) s[kh][i] = -__builtin_inff();
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(s[kh][i] * c2);
-        s[kh][i] = pv;
-        dp[kh][i] = pv * dp[kh][i];
-      }
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float tp[8], td[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          tp[j] = s[kh][8 * kb + j];
-          td[j] = dp[kh][8 * kb + j];
-        }
-        pb[kh][kb] = pack8<DT>(tp);
-        db[kh][kb] = pack8<DT>(td);
-      }
-    }
-    {
-      // dV^T += dO^T P and dK^T += Q^T dS for both halves; the next tile's
-      // row statistics are loaded in between.
-      u32x4 to[2], tq[2];
-      auto ld_t = [&](int i, int slot) {
-        const int dt = i >> 1, kb = i & 1;
-        const uint32_t t0 = b_t ^ tr_xor<DP>(dt, kb, 0);
-        const uint32_t t1 = b_t ^ tr_xor<DP>(dt, kb, 1);
-        to[slot] = cat2(lds_read_tr(Ob, t0), lds_read_tr(Ob, t1));
-        tq[slot] = cat2(lds_read_tr(Qb, t0), lds_read_tr(Qb, t1));
-      };
-      ld_t(0, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * ND; ++i) {
-        const int dt = i >> 1, kb = i & 1;
-        if (i + 1 < 2 * ND) ld_t(i + 1, (i + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        if (i == 0)
-          mfma_agpr<DT, true>(dv_acc[0][dt], as_vec8<DT>(to[i & 1]), pb[0][kb]);
-        else
-          mfma_agpr<DT, false>(dv_acc[0][dt], as_vec8<DT>(to[i & 1]), pb[0][kb]);
-        mfma_agpr<DT, false>(dk_acc[0][dt], as_vec8<DT>(tq[i & 1]), db[0][kb]);
-        mfma_agpr<DT, false>(dv_acc[1][dt], as_vec8<DT>(to[i & 1]), pb[1][kb]);
-        mfma_agpr<DT, false>(dk_acc[1][dt], as_vec8<DT>(tq[i & 1]), db[1][kb]);
-        load_stat(i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-    // dS (query-major, keys of each 16-key block in group order 0, 2, 1, 3)
-#pragma unroll
-    for (int kh = 0; kh < 2; ++kh) {
-      const int pos = ds_pos(64 * w + 32 * kh + r);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 words = __builtin_bit_cast(u32x4, db[kh][kb]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * kb + j;
-          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-          *(uint16_t*)(dSs + swz_ds<DP>(qi, pos)) = (uint16_t)(words[j >> 1] >> (16 * (j & 1)));
-        }
-      }
-    }
-    __syncthreads();  // dS complete; every wave is done with this query tile
-    if (more) store_q();
-
-    {
-      // dQ[q][32w + n] = sum_kv dS[q][kv] K[kv][32w + n]: 32x32x16 products,
-      // A = dS rows (one 16-byte read), B = K^T through two transpose reads.
-      int kv_act = lk - k0;
-      if (kv_act > BK) kv_act = BK;
-      if (causal && q0 + BQ + off - k0 < kv_act) kv_act = q0 + BQ + off - k0;
-      const int nst = (kv_act + 15) / 16;
-      dq = f32x16{};
-      // Reads run two steps ahead (three slots); the reads for steps past the
-      // last are clamped to a step inside the tiles and unused.
-      u32x4 kt[3], da[3];
-      auto ld_q = [&](int st, int slot) {
-        st = min(st, BK / 16 - 1);
-        kt[slot] = cat2(lds_read_tr(Kt, (b_t ^ tr_chunk<DP>(w, 0)) + tr_row<DP>(st, 0)),
-                        lds_read_tr(Kt, (b_t ^ tr_chunk<DP>(w, 1)) + tr_row<DP>(st, 1)));
-        da[slot] = *(const u32x4*)(dSs + swz_ds<DP>(r, 16 * st + 8 * h));
-      };
-      ld_q(0, 0);
-      ld_q(1, 1);
-      for (int st = 0; st < nst; st += 3) {
-        ld_q(st + 2, 2);
-        __builtin_amdgcn_sched_barrier(0);
-        dq = DT::mfma(as_vec8<DT>(da[0]), as_vec8<DT>(kt[0]), dq);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 >= nst) break;
-        ld_q(st + 3, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        dq = DT::mfma(as_vec8<DT>(da[1]), as_vec8<DT>(kt[1]), dq);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 2 >= nst) break;
-        ld_q(st + 4, 1);
-        __builtin_amdgcn_sched_barrier(0);
-        dq = DT::mfma(as_vec8<DT>(da[2]), as_vec8<DT>(kt[2]), dq);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      hq_p = hq;
-      q0_p = q0;
-      setup_dq(true);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) atomic_dq(j);
-    }
-    __syncthreads();  // next query tile visible; dS reads done
-    hq = hq_n;
-    q0 = q0_n;
-  }
-  // Epilogue: this lane's key rows of dK (scaled) and dV; rows past lk
-  // dropped.  The wait states between the last accumulating product and the
-  // reads of its AGPRs (more than a 32x32 product's 16 passes) are explicit.
-  asm volatile("s_nop 15\n\ts_nop 15" ::: "memory");
-  const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
-  const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
-#pragma unroll
-  for (int kh = 0; kh < 2; ++kh) {
-    const uint32_t krow = (uint32_t)(64 * w + 32 * kh + r) * kvrow_bytes;
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int dd = 32 * dt + 8 * gq + 4 * h;
-        if (dd < p.d) {
-          u32x2 ok, ov;
-          ok[0] = (uint32_t)DT::bits(dk_acc[kh][dt][4 * gq + 0] * p.scale) |
-                  ((uint32_t)DT::bits(dk_acc[kh][dt][4 * gq + 1] * p.scale) << 16);
-          ok[1] = (uint32_t)DT::bits(dk_acc[kh][dt][4 * gq + 2] * p.scale) |
-                  ((uint32_t)DT::bits(dk_acc[kh][dt][4 * gq + 3] * p.scale) << 16);
-          ov[0] = (uint32_t)DT::bits(dv_acc[kh][dt][4 * gq + 0]) |
-                  ((uint32_t)DT::bits(dv_acc[kh][dt][4 * gq + 1]) << 16);
-          ov[1] = (uint32_t)DT::bits(dv_acc[kh][dt][4 * gq + 2]) |
-                  ((uint32_t)DT::bits(dv_acc[kh][dt][4 * gq + 3]) << 16);
-          buf_store8(ok, dk_rs, krow + 2u * dd, 0);
-          buf_store8(ov, dv_rs, krow + 2u * dd, 0);
-        }
-      }
-  }
-}
-
-// ---------------------------------------------------------------------------
 // post: dq = scale * dq_acc in the storage dtype; zero pad rows of dk / dv.
 // ---------------------------------------------------------------------------
 template <class DT, int DP>
@@ -1082,10 +670,7 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   }
   if ((em = mark(1)) != hipSuccess) return em;
   if (bp.n_main > 0) {
-    if constexpr (DP == 128)
-      hipLaunchKernelGGL((thd_bwd_main4_kernel<DT>), dim3(bp.n_main), dim3(256), 0, s, bp);
-    else
-      hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(512), 0, s, bp);
+    hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(512), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
