@@ -105,11 +105,15 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
                    blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
-  // Pairs in row-major order (pair = row * h_q + head), so that o, dout and
-  // the accumulator rows cleared are each one stream.
+  // A workgroup covers PB consecutive rows of one head; consecutive
+  // workgroups take the heads of one row block in turn, so that together
+  // they stream the block's rows of o, dout and the accumulator, and each
+  // writes its rows' statistics ([h_q][T_q]) as one contiguous run.
   constexpr int KCH = DP / 8, PB = kPairsPerBlock<DP>;
   const int64_t pairs = p.T_q * p.h_q;
-  const int64_t p0 = (int64_t)((int)blockIdx.x - p.n_sched) * PB;
+  const int64_t bb = (int64_t)((int)blockIdx.x - p.n_sched);
+  const int64_t rb = bb / p.h_q;
+  const int head = (int)(bb - rb * p.h_q);
   const int g = threadIdx.x / KCH;
   const int c = threadIdx.x % KCH;
   // Every row is processed, pad rows included: the main kernel reads -D and
@@ -122,9 +126,9 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   // All loads first (the LSE too), so that each wave has them in flight at once.
 #pragma unroll
   for (int t = 0; t < 2; ++t) {
-    pr[t] = p0 + g + t * (PB / 2);
-    const int64_t row = pr[t] / p.h_q;
-    si[t] = (pr[t] - row * p.h_q) * p.T_q + row;  // statistics: [h_q][T_q]
+    const int64_t row = rb * PB + g + t * (PB / 2);
+    pr[t] = row < p.T_q ? row * p.h_q + head : pairs;  // pairs: past the end
+    si[t] = (int64_t)head * p.T_q + row;              // statistics: [h_q][T_q]
     a[t] = gr[t] = u32x4{0u, 0u, 0u, 0u};
     if (pr[t] < pairs && 8 * c < p.d) {
       const int64_t off = pr[t] * p.d + 8 * c;  // o, dout: [T_q][h_q][d]
@@ -662,7 +666,8 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   hipError_t em = mark(0);
   if (em != hipSuccess) return em;
   const int64_t n_pair_blocks = (bp.T_q * bp.h_q + kPairsPerBlock<DP> - 1) / kPairsPerBlock<DP>;
-  const int64_t n_pre = bp.n_sched + n_pair_blocks;
+  const int64_t n_pre =
+      bp.n_sched + (bp.T_q + kPairsPerBlock<DP> - 1) / kPairsPerBlock<DP> * bp.h_q;
   if (n_pre > 0) {
     hipLaunchKernelGGL((thd_bwd_pre_kernel<DT, DP>), dim3((unsigned)n_pre), dim3(256), 0, s, bp);
     hipError_t e = hipGetLastError();
