@@ -427,4 +427,55 @@ __device__ void build_schedule(const Model& md, int batch, int cap, int32_t* sch
   }
 }
 
+// Schedule grouped by sequence: sequences in decreasing order of their
+// largest tile's work (ties in sequence order, so the order matches
+// build_schedule's wherever a sequence's tiles all have the same work), each
+// sequence's tiles together and largest first (W(t) is monotone in t: descending t when the slope is positive,
+// ascending otherwise or without a causal mask).  Every tile of a sequence
+// and head then runs at about the same time on the XCD that the head fixes,
+// so tiles that walk the same rows of the other operand share them in L2.
+// Same output as build_schedule; one wave per sequence.
+template <class Model>
+__device__ __forceinline__ int seq_max_work(const SeqSummary& s) {
+  if (s.x <= 0) return -1;
+  if (!s.causal) return s.H;
+  return clampi(Model::kSlope > 0 ? Model::kSlope * (s.x - 1) + s.c : s.c, 0, s.H);
+}
+
+__device__ __forceinline__ int wave_sum_int(int v) {
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+
+template <class Model>
+__device__ void build_schedule_by_sequence(const Model& md, int batch, int cap, int32_t* sched,
+                                           int wave_id) {
+  const int lane = lane_id();
+  const int b = uniform(wave_id);
+  if (b >= batch) return;
+  const SeqSummary sb = md.seq(b);
+  const int wb = seq_max_work<Model>(sb);
+  int before = 0, total = 0;  // tiles of the sequences ahead of b; all tiles
+  for (int c0 = 0; c0 < batch; c0 += 64) {
+    const int j = c0 + lane;
+    SeqSummary sj = {0, 0, 0, false};
+    if (j < batch) sj = md.seq(j);
+    const int wj = seq_max_work<Model>(sj);
+    const bool ahead = j < batch && (wj > wb || (wj == wb && j < b));
+    before += wave_sum_int(ahead ? sj.x : 0);
+    total += wave_sum_int(sj.x);
+  }
+  const bool descending = sb.causal && Model::kSlope > 0;
+  for (int t = lane; t < sb.x; t += 64) {
+    const int rank = before + (descending ? sb.x - 1 - t : t);
+    if (rank < cap) {
+      int2 e;
+      e.x = b;
+      e.y = t;
+      *(int2*)(sched + 2 + 2 * rank) = e;
+    }
+  }
+  if (b == 0 && lane == 0) sched[0] = min(total, cap);
+}
+
 }  // namespace thd

@@ -10,9 +10,11 @@
 // mask tensor is read and the host never synchronises.
 //
 // One workgroup = 4 waves = one (sequence, 128-row query tile, query head)
-// work item.  A pre pass ranks the (sequence, query tile) items by the number
-// of key tiles they walk, largest first, and the attention workgroups take
-// them in that order, query heads minor.  Each wave owns 32
+// work item.  A pre pass orders the (sequence, query tile) items by sequence
+// (sequences by the key tiles their largest item walks, largest first) and,
+// within a sequence, largest item first; the attention workgroups take them
+// in that order, query heads minor, so that all query tiles of a sequence and
+// head run together and share its K and V in L2.  Each wave owns 32
 // query rows.  Scores are computed transposed, S^T = K Q^T, so that a lane
 // owns one query row: the row max needs one exchange between wave halves and
 // the probabilities land directly in the B-operand layout of O^T = V^T P^T.
@@ -60,7 +62,8 @@ struct FwdParams {
   int32_t* sched;   // [2 + 2 * n_tiles]: item count, then (sequence, tile) by rank
 };
 
-// Schedule of the attention workgroups (largest first, see build_schedule):
+// Schedule of the attention workgroups (grouped by sequence, largest tile
+// first, see build_schedule_by_sequence):
 // query tile t of sequence b walks W = ceil(lk / BN) key tiles, or, with a
 // causal mask type, the tiles up to its last row's diagonal:
 // W = ceil(clamp(min(lk, (t + 1) BM + off), 0) / BN) = clamp(a t + a + ceil(off / BN), 0, ceil(lk / BN))
@@ -120,7 +123,7 @@ __device__ void fwd_zero_pad_rows(const FwdParams& p, int zb) {
 template <int BN>
 __global__ __launch_bounds__(256) void thd_fwd_pre_kernel(FwdParams p) {
   if ((int)blockIdx.x < p.n_sched) {
-    build_schedule(FwdSchedModel<BN>{p}, p.batch, p.n_tiles, p.sched,
+    build_schedule_by_sequence(FwdSchedModel<BN>{p}, p.batch, p.n_tiles, p.sched,
                    blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
