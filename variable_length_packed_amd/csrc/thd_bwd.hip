@@ -11,9 +11,10 @@
 //
 // Three launches:
 //   pre  : -D per (row, head), zeroing of the fp32 dQ accumulator, and the
-//          main kernel's schedule (key tiles ranked by their work);
+//          main kernel's schedule (key tiles grouped by sequence, each
+//          sequence's largest first);
 //   main : one workgroup of 8 waves per (sequence, 256-key tile, kv head),
-//          largest first; wave w owns 32 keys and keeps dK^T and dV^T in
+//          in schedule order; wave w owns 32 keys and keeps dK^T and dV^T in
 //          registers (K and V sit in LDS) while the workgroup walks the
 //          32-row query tiles (from the diagonal when causal) of every query
 //          head of its GQA group.  dQ of a query tile is computed by the
@@ -65,7 +66,8 @@ struct BwdParams {
 // pre: -D = -rowsum(dO * O) in fp32, -LSE / scale, and dq_acc = 0; DP / 8 lanes
 // per (row, head).
 // ---------------------------------------------------------------------------
-// Schedule of the main kernel (largest first, see build_schedule): key tile
+// Schedule of the main kernel (grouped by sequence, largest tile first, see
+// build_schedule_by_sequence): key tile
 // kt of sequence b walks W = ceil(lq / BQ) query tiles, or, with a causal
 // mask type, those from the first one that sees key kt * BK:
 // W = clamp(ceil(lq / BQ) - 8 kt + ceil(off / BQ), 0, ceil(lq / BQ))
@@ -101,7 +103,7 @@ constexpr int kPairsPerBlock = 2 * 256 / (DP / 8);
 template <class DT, int DP>
 __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
   if ((int)blockIdx.x < p.n_sched) {
-    build_schedule(BwdSchedModel{p, (int64_t)p.h_q * DP * 4}, p.batch, p.n_kv_tiles, p.sched,
+    build_schedule_by_sequence(BwdSchedModel{p, (int64_t)p.h_q * DP * 4}, p.batch, p.n_kv_tiles, p.sched,
                    blockIdx.x * 4 + (int)(threadIdx.x >> 6));
     return;
   }
@@ -225,7 +227,9 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   unsigned char* Ob = smem + OFF_DO;
   unsigned char* dSs = smem + OFF_DS;
 
-  // Workgroups in schedule order (largest items first), kv heads minor.
+  // Workgroups in schedule order (by sequence, largest items first), kv heads
+  // minor: the key tiles of a (sequence, head) run together on one XCD and
+  // share its Q, dO and row statistics in L2.
   const int bid = blockIdx.x;
   const int rk = bid / p.h_kv;
   const int hk = bid - rk * p.h_kv;
