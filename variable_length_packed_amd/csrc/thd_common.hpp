@@ -338,16 +338,17 @@ __device__ __forceinline__ int ceil_div_pos(int a, int b) { return a > 0 ? (a + 
 __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? lo : (x > hi ? hi : x); }
 
 // ---------------------------------------------------------------------------
-// Largest-first schedules.  The tiles (sequence b, tile t) of a kernel are
-// ranked by their work W, largest first, ties in (b, t) order, and rank r is
-// run by the workgroups r * heads .. r * heads + heads - 1, so the longest
-// workgroups start first and the short ones fill in behind them (greedy list
-// scheduling in decreasing order).  A rank is a count,
-//   rank = #{tiles with larger W} + #{equal W, earlier (b, t)},
-// and each sequence's share of both counts has a closed form: a sequence has
-// x tiles, and W(t) = H for all of them (no causal mask) or
-// W(t) = clamp(a t + c, 0, H) with the model's slope a (causal).  A Model
-// gives md.seq(b) = {x, c, H, causal} and kSlope.
+// Work schedules.  The tiles (sequence b, tile t) of a kernel have work W(t)
+// in closed form from the lengths and the mask type: W(t) = H for all x
+// tiles of a sequence (no causal mask) or W(t) = clamp(a t + c, 0, H) with
+// the model's slope a (causal).  A Model gives md.seq(b) = {x, c, H, causal}
+// and kSlope.  The schedule lists the tiles grouped by sequence, sequences
+// in decreasing order of their largest tile's work (ties in sequence order),
+// each sequence's tiles largest first; rank r is run by the workgroups
+// r * heads .. r * heads + heads - 1.  The longest tiles still start first
+// and short ones fill in behind them, and every tile of a sequence and head
+// runs at about the same time on the XCD that the head fixes, so tiles that
+// walk the same rows of the other operand share them in L2.
 // Output: sched[0] = number of tiles kept (at most cap), then (b, t) of rank
 // r at sched[2 + 2r], sched[3 + 2r].  One wave per sequence (wave_id = b);
 // its lanes take t = lane, lane + 64, ...; the wave of sequence 0 also
@@ -359,82 +360,7 @@ struct SeqSummary {
   bool causal;
 };
 
-// #{t in [0, x) : clamp(a t + c, 0, H) > w} for w >= 0, a != 0
-__device__ __forceinline__ int count_gt_lin(int x, int a, int c, int H, int w) {
-  if (x <= 0 || H <= w) return 0;
-  // with H > w >= 0 the clamp keeps W(t) > w exactly when a t + c > w
-  if (a > 0) return x - clampi(floor_div(w - c, a) + 1, 0, x);
-  return clampi(ceil_div(c - w, -a), 0, x);
-}
-__device__ __forceinline__ int count_ge_lin(int x, int a, int c, int H, int w) {
-  return w <= 0 ? x : count_gt_lin(x, a, c, H, w - 1);
-}
-
-template <class Model>
-struct SchedCounts {
-  static __device__ int work(const SeqSummary& s, int t) {
-    return s.causal ? clampi(Model::kSlope * t + s.c, 0, s.H) : s.H;
-  }
-  static __device__ int gt(const SeqSummary& s, int w) {
-    if (!s.causal) return s.H > w ? s.x : 0;
-    return count_gt_lin(s.x, Model::kSlope, s.c, s.H, w);
-  }
-  static __device__ int eq_below(const SeqSummary& s, int n, int w) {  // among t < n
-    if (!s.causal) return s.H == w ? n : 0;
-    return count_ge_lin(n, Model::kSlope, s.c, s.H, w) - count_gt_lin(n, Model::kSlope, s.c, s.H, w);
-  }
-};
-
-template <class Model>
-__device__ void build_schedule(const Model& md, int batch, int cap, int32_t* sched, int wave_id) {
-  typedef SchedCounts<Model> C;
-  const int lane = lane_id();
-  const int b = uniform(wave_id);
-  if (b >= batch) return;
-  const SeqSummary sb = md.seq(b);
-  const bool counter = b == 0;
-  int rounds = (sb.x + 63) / 64;
-  if (counter && rounds == 0) rounds = 1;
-  for (int rd = 0; rd < rounds; ++rd) {
-    const int t = 64 * rd + lane;
-    const int w = C::work(sb, t);  // unused when t >= x
-    int64_t rank = C::eq_below(sb, t < sb.x ? t : 0, w);
-    int64_t total = 0;
-    for (int c0 = 0; c0 < batch; c0 += 64) {
-      // lane j summarises sequence c0 + j; every lane then visits all of them
-      SeqSummary sj = {0, 0, 0, false};
-      if (c0 + lane < batch) sj = md.seq(c0 + lane);
-      const int px = sj.x, pc = sj.c, ph = (sj.H << 1) | (sj.causal ? 1 : 0);
-      const int n = min(64, batch - c0);
-      for (int j = 0; j < n; ++j) {
-        SeqSummary o;
-        o.x = __builtin_amdgcn_readlane(px, j);
-        o.c = __builtin_amdgcn_readlane(pc, j);
-        const int hv = __builtin_amdgcn_readlane(ph, j);
-        o.H = hv >> 1;
-        o.causal = (hv & 1) != 0;
-        rank += C::gt(o, w) + (c0 + j < b ? C::eq_below(o, o.x, w) : 0);
-        total += o.x;
-      }
-    }
-    if (t < sb.x && rank < cap) {  // ranks are a permutation of [0, total)
-      int2 e;
-      e.x = b;
-      e.y = t;
-      *(int2*)(sched + 2 + 2 * rank) = e;
-    }
-    if (counter && rd == 0 && lane == 0) sched[0] = (int)min(total, (int64_t)cap);
-  }
-}
-
-// Schedule grouped by sequence: sequences in decreasing order of their
-// largest tile's work (ties in sequence order, so the order matches
-// build_schedule's wherever a sequence's tiles all have the same work), each
-// sequence's tiles together and largest first (W(t) is monotone in t: descending t when the slope is positive,
-// ascending otherwise or without a causal mask).  Every tile of a sequence
-// and head then runs at about the same time on the XCD that the head fixes,
-// so tiles that walk the same rows of the other operand share them in L2.
-// Same output as build_schedule; one wave per sequence.
+// Work of a sequence's largest tile (-1 for a sequence without tiles).
 template <class Model>
 __device__ __forceinline__ int seq_max_work(const SeqSummary& s) {
   if (s.x <= 0) return -1;
@@ -442,11 +368,14 @@ __device__ __forceinline__ int seq_max_work(const SeqSummary& s) {
   return clampi(Model::kSlope > 0 ? Model::kSlope * (s.x - 1) + s.c : s.c, 0, s.H);
 }
 
+// Sum of v over the 64 lanes of the wave, in every lane (all lanes active).
 __device__ __forceinline__ int wave_sum_int(int v) {
   for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
   return v;
 }
 
+// The schedule described above; sequence b's wave counts the tiles of the
+// sequences ahead of b and writes b's tiles after them.
 template <class Model>
 __device__ void build_schedule_by_sequence(const Model& md, int batch, int cap, int32_t* sched,
                                            int wave_id) {
