@@ -150,12 +150,15 @@ __global__ __launch_bounds__(256, DP > 32 ? 3 : 2) void thd_fwd_kernel(FwdParams
   // buffer j: K tile at 2j * TILE, V tile at (2j + 1) * TILE
   __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TILE];
 
-  // Workgroups in schedule order (largest items first), query heads minor:
-  // with h_q a multiple of 8, head hq always lands on XCD hq % 8, whose L2
-  // then holds that head's K and V.
+  // Workgroups in schedule order, heads minor.  Slot s of a rank takes kv
+  // head s % h_kv and query head (s % h_kv) * group + s / h_kv of its group:
+  // with h_kv a multiple of 8, every query head of kv head hk then lands on
+  // XCD hk % 8 (the workgroup id modulo 8), whose L2 holds that head's K and
+  // V for all of them.  (Without GQA this is query head s.)
   const int bid = blockIdx.x;
   const int rk = bid / p.h_q;
-  const int hq = bid - rk * p.h_q;
+  const int slot = bid - rk * p.h_q;
+  const int hq = (slot % p.h_kv) * p.group + slot / p.h_kv;
   if (rk >= p.sched[0]) return;
   const int b = uniform(p.sched[2 + 2 * rk]);
   const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
