@@ -265,17 +265,24 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
   const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
   const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
+  // Straight from memory into LDS: load i of wave w fills 1 KB block
+  // 8i + w of each tile, lane l the 16-byte slot 64(8i + w) + l, i.e. row
+  // slot / KCH at swizzled chunk position slot % KCH, which holds the row's
+  // memory chunk (slot % KCH) ^ f(row).  Waited for before the barrier below.
   {
-    const rsrc_t k_rs = make_rsrc(kbase, kv_bytes);
-    const rsrc_t v_rs = make_rsrc(vbase, kv_bytes);
+    static_assert(BK * KCH % 512 == 0, "whole 1 KB blocks per wave");
+    const u32x4 k_rs = rsrc_words(kbase, kv_bytes);
+    const u32x4 v_rs = rsrc_words(vbase, kv_bytes);
+    const uint32_t k_lds = lds_addr(Kt), v_lds = lds_addr(Vt);
 #pragma unroll
     for (int i = 0; i < BK * KCH / 512; ++i) {
-      const int cid = tid + 512 * i;
-      const int row = cid / KCH;
-      const int x = cid - row * KCH;
-      const uint32_t off = 8 * x < p.d ? (uint32_t)row * kvrow_bytes + 16u * x : kOobOffset;
-      *(u32x4*)(Kt + swz<DP>(row, 8 * x)) = buf_load16(k_rs, off, 0);
-      *(u32x4*)(Vt + swz<DP>(row, 8 * x)) = buf_load16(v_rs, off, 0);
+      const int slot = 64 * (8 * i + w) + l;
+      const int row = slot / KCH;
+      const int x = slot - row * KCH;
+      const int gc = x ^ (int)((swz<DP>(row, 0) >> 4) & (KCH - 1));
+      const uint32_t off = 8 * gc < p.d ? (uint32_t)row * kvrow_bytes + 16u * gc : kOobOffset;
+      buf_load_lds16(k_rs, k_lds + 1024u * (8 * i + w), off);
+      buf_load_lds16(v_rs, v_lds + 1024u * (8 * i + w), off);
     }
   }
 
@@ -411,6 +418,9 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
     load_q(hq, q0, true);
     store_q();
   }
+  // vmcnt(0): this wave's K and V blocks are in LDS (the compiler does not
+  // count those loads), and so are the first tile's statistics.
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();  // K, V and the first query tile visible
   for (int iter = 0; iter < n_iter; ++iter) {
     const bool more = iter + 1 < n_iter;
