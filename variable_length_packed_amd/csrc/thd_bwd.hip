@@ -611,15 +611,17 @@ __global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
 // post: dq = scale * dq_acc in the storage dtype; zero pad rows of dk / dv.
 // ---------------------------------------------------------------------------
 template <class DT, int DP>
-__global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int n_conv_wg) {
+__global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int n_zero_wg) {
   const int tid = threadIdx.x;
-  if ((int)blockIdx.x < n_conv_wg) {
+  // The pad-row workgroups come first: each starts with a dependent search of
+  // the sequence starts, whose latency the conversion stream behind it covers.
+  if ((int)blockIdx.x >= n_zero_wg) {
     // (row, head) pairs in row-major order, like the pre pass: pair pr sits
     // at pr * DP in the accumulator and at pr * d in dq, so each thread reads
     // and writes chunk c of two pairs of one stream each.
     constexpr int KCH = DP / 8, PB = kPairsPerBlock<DP>;
     const int64_t pairs = p.T_q * p.h_q;
-    const int64_t p0 = (int64_t)blockIdx.x * PB;
+    const int64_t p0 = (int64_t)((int)blockIdx.x - n_zero_wg) * PB;
     const int g = tid / KCH;
     const int c = tid % KCH;
     if (8 * c >= p.d) return;
@@ -650,7 +652,7 @@ __global__ __launch_bounds__(256) void thd_bwd_post_kernel(BwdParams p, int n_co
     return;
   }
   __shared__ uint8_t invalid[kZeroRowsB];
-  const int64_t r0 = (int64_t)(blockIdx.x - n_conv_wg) * kZeroRowsB;
+  const int64_t r0 = (int64_t)blockIdx.x * kZeroRowsB;
   int mine = 0;
   if (tid < kZeroRowsB) {
     const int64_t rr = r0 + tid;
@@ -698,7 +700,7 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   const int64_t n_zero = (bp.T_kv + kZeroRowsB - 1) / kZeroRowsB;
   if (n_conv + n_zero > 0) {
     hipLaunchKernelGGL((thd_bwd_post_kernel<DT, DP>), dim3((unsigned)(n_conv + n_zero)), dim3(256), 0,
-                       s, bp, (int)n_conv);
+                       s, bp, (int)n_zero);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
