@@ -109,21 +109,18 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
 // with the mirrored lane of the half row (8 lanes) and of the row (16 lanes).
 // Each step adds two partial sums in either order, so all lanes of a group
 // end with the same value.  Every lane of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float add_dpp(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false);
+  return v + __builtin_bit_cast(float, o);
+}
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   static_assert(N == 4 || N == 8 || N == 16, "DPP rows hold 16 lanes");
-  auto step = [](float v, int ctrl) {
-    const int o = ctrl == 0xB1   ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)
-                  : ctrl == 0x4E ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)
-                  : ctrl == 0x141
-                      ? __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)
-                      : __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false);
-    return v + __builtin_bit_cast(float, o);
-  };
-  x = step(x, 0xB1);
-  x = step(x, 0x4E);
-  if (N >= 8) x = step(x, 0x141);
-  if (N >= 16) x = step(x, 0x140);
+  x = add_dpp<0xB1>(x);                   // quad_perm [1,0,3,2]
+  x = add_dpp<0x4E>(x);                   // quad_perm [2,3,0,1]
+  if constexpr (N >= 8) x = add_dpp<0x141>(x);   // row_half_mirror
+  if constexpr (N >= 16) x = add_dpp<0x140>(x);  // row_mirror
   return x;
 }
 
