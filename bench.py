@@ -15,8 +15,12 @@ would otherwise make the timed steps depend on what ran before them.
 
 Prints one JSON line.  `value` is valid-pair TFLOP/s of fwd+bwd (14*d FLOPs
 per valid (query, key) pair and head); `roofline` describes the dominant
-kernel, timed with HIP events on the stream it runs on; `cpu_baseline` is the
-fp64 oracle timed on the host on a bounded sample of the same workload.
+kernel, timed with HIP events on the stream it runs on (its `traffic`, and
+the `counters` object -- MFMA busy, LDS active and HBM bytes of the attention
+kernels -- come from the committed rocprofv3 records of this workload, and
+are null once a kernel's sources differ from those the records were taken
+on); `cpu_baseline` is the fp64 oracle timed on the host on a bounded sample
+of the same workload.  Other workloads: --config 3..7, --fwd-only, --cp N.
 """
 import argparse
 import json
