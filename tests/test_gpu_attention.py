@@ -72,6 +72,16 @@ SMALL = [
          cross=True, slot_multiple=64, gap_before=2),
     dict(seed=113, batch=8, max_len=140, h_q=2, d=32, dtype="bf16", causal="types",
          cross=True, extra_cu=2, min_len=0),
+    # head dims below their tile width (16 of 32, 48 of 64, 80 and 120 of 128),
+    # an odd kv-head count and a group of 2
+    dict(seed=114, batch=5, max_len=300, h_q=6, h_kv=3, d=48, dtype="bf16", causal="types",
+         cross=True, slot_multiple=32, gap_before=1),
+    dict(seed=115, batch=6, max_len=280, h_q=3, h_kv=3, d=80, dtype="fp16", causal="mixed",
+         extra_cu=1),
+    dict(seed=116, batch=4, max_len=350, h_q=2, h_kv=1, d=120, dtype="bf16", causal="all",
+         slot_multiple=128, gap_before=2),
+    dict(seed=117, batch=7, max_len=190, h_q=4, h_kv=2, d=16, dtype="fp16", causal="types",
+         cross=True, min_len=0),
 ]
 
 
