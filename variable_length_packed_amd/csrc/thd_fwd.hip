@@ -30,14 +30,17 @@ namespace thd {
 namespace {
 
 constexpr int kFwdBM = 128;  // query rows per workgroup
-// Keys per LDS tile and tiles in flight.  At d > 32 the tiles hold 32 keys in
-// three stages (48 KB per workgroup at d = 128), so that three workgroups, or
-// three waves per SIMD, share a CU; at d <= 32 a 32-key tile would be smaller
-// than one 1 KB load per wave, and 64-key tiles in two stages are kept.
+// Keys per LDS tile and tiles in flight.  At d > 32 the tiles hold 32 keys,
+// and three workgroups (three waves per SIMD) share a CU.  At d = 128 two
+// stages (32 KB per workgroup) ran the forward about 1 % faster than three
+// (48 KB) on short and long causal sequences alike, and 64-key tiles in two
+// stages (two workgroups per CU) about 4.5 % slower; d = 64 keeps three
+// stages.  At d <= 32 a 32-key tile would be smaller than one 1 KB load per
+// wave, and 64-key tiles in two stages are kept.
 template <int DP>
 struct FwdTile {
   static constexpr int BN = DP > 32 ? 32 : 64;
-  static constexpr int NS = DP > 32 ? 3 : 2;
+  static constexpr int NS = DP == 128 ? 2 : DP > 32 ? 3 : 2;
 };
 constexpr int kWaveM = 32;   // query rows per wave
 constexpr int kZeroRows = 64;
