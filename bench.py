@@ -20,7 +20,7 @@ the `counters` object -- MFMA busy, LDS active and HBM bytes of the attention
 kernels -- come from the committed rocprofv3 records of this workload, and
 are null once a kernel's sources differ from those the records were taken
 on); `cpu_baseline` is the fp64 oracle timed on the host on a bounded sample
-of the same workload.  Other workloads: --config 3..7, --fwd-only, --cp N.
+of the same workload.  Other workloads: --config 3..7, --fwd-only.
 """
 import argparse
 import json
@@ -48,10 +48,6 @@ def parse():
                     help="time the padding masks and the forward only, against the HBM "
                          "roofline (for the split-KV decode workload)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--cp", type=int, default=0,
-                    help="context parallelism over this many ranks, emulated on the one GPU: "
-                         "every rank's share (its forward and backward ring steps, the merges "
-                         "and the gradient sums) timed in turn; the ring's sends are not run")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="only run a plain device copy of this many MiB (read + write) a few "
                          "times, to calibrate the FETCH_SIZE / WRITE_SIZE counters")
@@ -67,10 +63,12 @@ KERNEL_SOURCES = {
 
 
 def source_digest(kernel):
-    """Digest of the HIP sources of one kernel; its counter-based traffic is
-    valid only for them."""
+    """Digest of the HIP sources of one kernel and of the compiler flags they
+    are built with; its counter-based traffic is valid only for them."""
     import hashlib
+    from variable_length_packed_amd.build import compile_flags
     h = hashlib.sha256()
+    h.update(" ".join(f for f in compile_flags() if not f.startswith("-I")).encode())
     for name in KERNEL_SOURCES[kernel]:
         h.update(name.encode())
         with open(os.path.join(ROOT, "variable_length_packed_amd", "csrc", name), "rb") as f:
@@ -156,7 +154,7 @@ def cpu_baseline(w, q, k, v, do, budget_s):
     pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, heads)
     flops = 14 * w.d * pairs
     return {"value": flops / elapsed / 1e12, "unit": "TFLOP/s", "cores": int(threads),
-            "kind": "oracle",
+            "affinity_cores": len(os.sched_getaffinity(0)), "kind": "oracle",
             "sample": f"fp64 numpy oracle, fwd+bwd of {heads} head passes ({heads / w.h_q:.2f} "
                       f"times the {w.h_q} heads) over all {w.batch} sequences of the same "
                       f"workload ({flops / 1e9:.1f} GFLOP in {elapsed:.1f} s)"}
@@ -166,9 +164,6 @@ def main():
     a = parse()
     if a.copy_calibration_mib:
         copy_calibration(a.copy_calibration_mib)
-        return
-    if a.cp:
-        cp_bench(a)
         return
     if a.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
@@ -422,109 +417,6 @@ def fwd_only_result(a, w, timed, elapsed):
                      "avg_launch_ms": round(f_ms, 4)},
         "cpu_baseline": None,
     }
-
-
-def cp_bench(a):
-    """Context parallelism over a.cp ranks on one GPU: the workload's sequences
-    padded to multiples of 2 * cp and split (rank r: chunks r and 2cp-1-r),
-    every rank's fwd + bwd share (cp forward steps with their log-sum-exp
-    merges, cp backward steps with the fp32 sums of their dq) timed with HIP
-    events; the dk / dv contributions a ring would send back are left as the
-    per-step outputs.  The step of a cp-rank job takes as long as its slowest
-    rank, so value = all valid pairs' FLOPs / max over ranks of a rank's time.
-    Ring communication is not part of it."""
-    import numpy as np
-    import torch
-
-    import workloads
-    from variable_length_packed_amd import cp
-    from variable_length_packed_amd.metrics import attention_flops, valid_pairs
-
-    n = int(a.cp)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    w = workloads.config(a.config)
-    if not w.self_attention or w.cu_q_padded is not None:
-        sys.exit("bench.py --cp: needs a self-attention workload without padding gaps")
-    q, k, v, do = workloads.make_tensors(w, device=dev)
-    cu = torch.from_numpy(np.asarray(w.cu_q, np.int32)).to(dev)
-    mt = torch.from_numpy(np.asarray(w.causal, np.uint8)).to(dev)
-    # global padded layout: slot starts and row count from the device layout kernel
-    lay = cp.cp_layout(cu, n, 0, 0, cp.SIDE_Q, mask_type=mt, batch_size=w.batch)
-    gstart = lay["global_cu_seqlens_padded"].cpu().numpy().astype(np.int64)
-    T = int(gstart[-1])
-    src = np.concatenate([np.arange(gstart[b], gstart[b] + L) for b, L in enumerate(w.lens_q)])
-    idx = torch.from_numpy(src).to(dev)
-
-    def padded(x):
-        y = torch.zeros((T,) + tuple(x.shape[1:]), dtype=x.dtype, device=dev)
-        y[idx] = x[:len(src)]
-        return y
-
-    glob = [padded(t) for t in (q, k, v, do)]
-    shards = [[cp.cp_shard(t, cu, n, r, T // n, batch_size=w.batch) for r in range(n)]
-              for t in glob]
-    views = [cp.cp_views(cu, n, r, mask_type=mt, batch_size=w.batch) for r in range(n)]
-    max_len = int(np.max(w.lens_q))
-
-    def rank_step(r):
-        o, lse = cp.cp_attn_fwd(shards[0][r], shards[1], shards[2], cu, n, r, max_len,
-                                mask_type=mt, batch_size=w.batch, views=views[r])
-        cp.cp_attn_bwd(shards[0][r], shards[1], shards[2], o, shards[3][r], lse, cu, n, r,
-                       max_len, mask_type=mt, batch_size=w.batch, views=views[r])
-
-    t_spin = time.perf_counter()
-    while time.perf_counter() - t_spin < a.spinup_seconds:
-        for r in range(n):
-            rank_step(r)
-        torch.cuda.synchronize()
-    for _ in range(a.warmup):
-        for r in range(n):
-            rank_step(r)
-    torch.cuda.synchronize()
-    cur = torch.cuda.current_stream(dev)
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(n)] for _ in range(a.steps)]
-    t0 = time.perf_counter()
-    for i in range(a.steps):
-        for r in range(n):
-            ev[i][r][0].record(cur)
-            rank_step(r)
-            ev[i][r][1].record(cur)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    rank_ms = [sum(e[r][0].elapsed_time(e[r][1]) for e in ev) / a.steps for r in range(n)]
-    slow = max(rank_ms)
-    pairs = valid_pairs(w.lens_q, w.lens_kv, w.causal, w.h_q)
-    flops = attention_flops(pairs, w.d, "fwd+bwd")
-    value = flops / (slow * 1e-3) / 1e12
-    out = {
-        "metric": "packed-THD attention valid-pair TFLOP/s fwd+bwd, context parallel over "
-                  f"{n} ranks emulated on one GPU (slowest rank's share; ring sends not run)",
-        "value": round(value, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": a.steps,
-        "warmup": a.warmup,
-        "ms_per_step": round(slow, 4),
-        "higher_is_better": True,
-        "scaling": "strong",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "bf16" else "fp16",
-        "data": "synthetic",
-        "rank_ms": [round(x, 4) for x in rank_ms],
-        "all_ranks_ms_on_one_gpu": round(elapsed * 1e3 / a.steps, 4),
-        "config": {
-            "workload": f"config {w.name} split over {n} context-parallel ranks "
-                        f"({T} padded rows, {T // n} per rank), h_q={w.h_q} h_kv={w.h_kv} "
-                        f"d={w.d} {w.dtype}",
-            "tokens": int(w.T_q), "padded_tokens": T, "batch": w.batch,
-            "valid_pairs": int(pairs), "flops_per_step": int(flops), "seed": w.seed,
-        },
-        "roofline": None,
-        "cpu_baseline": None,
-    }
-    print(json.dumps(out), flush=True)
 
 
 if __name__ == "__main__":

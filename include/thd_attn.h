@@ -174,101 +174,6 @@ const char* thd_status_string(int status);
 /* Library version as major*10000 + minor*100 + patch. */
 int thd_version(void);
 
-/* ---------------------------------------------------------------------------
- * Context parallelism, the share of one rank (Megatron-LM issue "How to pad
- * sequences that cannot be evenly split in context parallelism (CP)?",
- * question and repro).  A sequence of valid length len_b is padded to
- * P_b = 2n * C_b rows, C_b = ceil(len_b / 2n) (the global layout: slots of P_b
- * rows, valid rows first), cut into 2n chunks of C_b rows; rank r holds
- * chunks r and 2n-1-r as one local slot of 2 C_b rows (its valid rows are a
- * prefix of the slot).  Rank r's attention is the merge, by log-sum-exp, of
- * one thd_attn_fwd per rank t (the KV ring; on one GPU all shards are local):
- * the call reads rank t's keys through the views thd_cp_layout describes and
- * uses its mask types (causal only for t == r).  n = cp_size.
- * ------------------------------------------------------------------------- */
-
-/* Metadata of one step's view, written on the device (no host sync).
- * side 0: rank `rank`'s queries for the step with peer `peer`; side 1: peer
- * `peer`'s keys for that step.  For a causal sequence (mask_type 1 or 2) the
- * query view of a step with peer > rank is the second local chunk only, and
- * the key view of a peer < rank is its first chunk only; otherwise a view is
- * the whole local slot.  Outputs (device, each may be NULL):
- * out_cu_seqlens[batch+1] (cumulative valid rows of the views),
- * out_cu_seqlens_padded[batch+1] (view starts in the owner's local layout;
- * entry batch = the owner's local rows), out_global_cu_seqlens_padded[batch+1]
- * (slot starts of the global layout; entry batch = its rows), out_mask_type
- * [batch] (causal only when peer == rank).  cu_seqlens and mask_type (NULL =
- * padding) have the thd_varlen_args meaning.  Errors: THD_ERR_SHAPE
- * (batch < 0, cp_size < 1, rank or peer outside [0, cp_size), side not 0/1),
- * THD_ERR_NULL, THD_ERR_HIP. */
-int thd_cp_layout(const int32_t* cu_seqlens, const uint8_t* mask_type, int32_t batch,
-                  int32_t cp_size, int32_t rank, int32_t peer, int32_t side,
-                  int32_t* out_cu_seqlens, int32_t* out_cu_seqlens_padded,
-                  int32_t* out_global_cu_seqlens_padded, uint8_t* out_mask_type, void* stream);
-
-/* Rank `rank`'s shard of a [total_global, row] tensor in the global padded
- * layout: local row l of sequence b's slot (starts from
- * local_cu_seqlens_padded, the side-0 view of the step peer == rank) copies
- * global row global_cu_seqlens_padded[b] + chunk * C_b + (l - start) % C_b,
- * chunk = rank for the first C_b rows, 2n-1-rank after.  row_bytes: bytes of
- * one row (h * head_dim * element size), a multiple of 16; src and dst 16-byte
- * aligned.  Rows outside every slot are not written.  Errors: THD_ERR_SHAPE,
- * THD_ERR_NULL, THD_ERR_UNSUPPORTED (alignment), THD_ERR_HIP. */
-int thd_cp_gather(const int32_t* cu_seqlens, const int32_t* local_cu_seqlens_padded,
-                  const int32_t* global_cu_seqlens_padded, int32_t batch, int32_t cp_size,
-                  int32_t rank, const void* src, int64_t total_global, void* dst,
-                  int64_t total_local, int32_t row_bytes, void* stream);
-
-/* Fold one partial attention output into an fp32 accumulator by
- * log-sum-exp: with a = lse_acc, b = lse_part (natural log, [h, total]),
- * lse_acc <- log(e^a + e^b) and o_acc <- (e^a o_acc + e^b o_part) / (e^a + e^b)
- * per (row, head), o_part in the storage dtype ([total, h, head_dim]),
- * o_acc fp32.  first != 0 takes the accumulator as empty (a = -inf).  A
- * -inf pair stays -inf with o = 0.  o_out (may be NULL) also receives the
- * merged o in the storage dtype (RNE).  Errors: THD_ERR_SHAPE (total < 0,
- * h <= 0, head_dim not a positive multiple of 8), THD_ERR_UNSUPPORTED (dtype,
- * alignment), THD_ERR_NULL, THD_ERR_HIP. */
-int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, float* lse_acc,
-                       void* o_out, int64_t total, int32_t h, int32_t head_dim, int32_t dtype,
-                       int32_t first, void* stream);
-
-/* Sum of partial gradients in fp32: acc[i] += src[i] for i < n_elems (first
- * != 0: acc[i] = src[i]), src in the storage dtype; out (may be NULL) also
- * receives the sum in the storage dtype (RNE).  Rank r's gradients are the
- * sums of one thd_attn_bwd per ring step (on the step's views, with the
- * merged o and lse of its queries): dq over the steps, and the dk / dv
- * contributions to each rank's shard over the ranks.  n_elems: a multiple of
- * 8; pointers 16-byte aligned.  Errors: THD_ERR_SHAPE, THD_ERR_UNSUPPORTED
- * (dtype, alignment), THD_ERR_NULL, THD_ERR_HIP. */
-int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int32_t dtype,
-                   int32_t first, void* stream);
-
-/* The log-sum-exp merge of n_parts (1..8) partial attention outputs in one
- * pass: with l_k = lse_parts[k] (natural log, [h, total]) and
- * m = max_k l_k per (row, head), lse_out = m + log(sum_k e^(l_k - m)) and
- * o_out = sum_k e^(l_k - lse_out) o_parts[k], in fp32, o_out written once in
- * the storage dtype (RNE).  A (row, head) whose partials are all -inf gets
- * lse -inf and o = 0.  o_parts[k] and o_out are [total, h, head_dim], 16-byte
- * aligned; lse_out may be NULL; o_out may not alias a partial.  This is how
- * rank r's output is formed from the forwards of its ring steps: reading
- * each step's output once, against twice per step for the fp32 accumulator
- * of thd_attn_lse_merge.  Errors: THD_ERR_SHAPE (total < 0, h <= 0,
- * head_dim not a positive multiple of 8, n_parts outside 1..8),
- * THD_ERR_UNSUPPORTED (dtype, alignment), THD_ERR_NULL, THD_ERR_HIP. */
-int thd_attn_lse_merge_n(const void* const* o_parts, const float* const* lse_parts,
-                         int32_t n_parts, void* o_out, float* lse_out, int64_t total, int32_t h,
-                         int32_t head_dim, int32_t dtype, void* stream);
-
-/* out[i] = sum_k parts[k][i] for i < n_elems, over n_parts (1..8) partials in
- * the storage dtype, added in fp32 in the order given and written once in the
- * storage dtype (RNE): the one-pass form of thd_accumulate, for rank r's dq
- * over its ring steps and a shard's dk / dv over the ranks.  n_elems: a
- * multiple of 8; pointers 16-byte aligned; out may not alias a partial.
- * Errors: THD_ERR_SHAPE, THD_ERR_UNSUPPORTED (dtype, alignment),
- * THD_ERR_NULL, THD_ERR_HIP. */
-int thd_sum_n(const void* const* parts, int32_t n_parts, void* out, int64_t n_elems,
-              int32_t dtype, void* stream);
-
 #ifdef __cplusplus
 }
 #endif

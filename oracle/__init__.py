@@ -5,10 +5,12 @@ the benchmark's CPU-baseline leg, never by the library itself.
 """
 from .thd_oracle import (  # noqa: F401
     attn_bwd,
+    attn_bwd_key_range,
     attn_fwd,
     attn_rows,
     padding_mask,
     padding_mask_loop,
+    round_to_storage,
     sequence_rows,
     valid_pairs,
     visible_keys,

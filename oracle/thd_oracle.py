@@ -55,6 +55,8 @@ __all__ = [
     "attn_fwd",
     "attn_bwd",
     "attn_rows",
+    "attn_bwd_key_range",
+    "round_to_storage",
 ]
 
 
@@ -246,15 +248,21 @@ def attn_fwd(q, k, v, cu_q, cu_kv, batch_size, mask_type=None,
 # ---------------------------------------------------------------------------
 
 def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, mask_type=None,
-             cu_q_padded=None, cu_kv_padded=None, scale=None):
+             cu_q_padded=None, cu_kv_padded=None, scale=None, out=None):
     """Gradients (dq, dk, dv) of sum(out * dout) for ``attn_fwd``.
 
     Textbook softmax-attention backward, per sequence and query head, with the
     probabilities recomputed from scratch:
-    dV = P^T dO;  dP = dO V^T;  dS = P * (dP - rowsum(P * dP));
+    dV = P^T dO;  dP = dO V^T;  dS = P * (dP - D),  D = rowsum(P * dP);
     dQ = scale dS K;  dK = scale dS^T Q.
     Key/value gradients of a GQA group are summed over its query heads.
     ``dout`` at pad rows is ignored and every pad row of dq/dk/dv is 0.
+
+    ``out``: the forward's output as a backward receives it (a backward call
+    takes the saved output as an input).  When given, D is rowsum(dO * out)
+    over those values -- equal to rowsum(P * dP) for the exact output, since
+    dO . O_i = sum_j P_ij (dO_i . V_j) -- so the effect of storing the output
+    in a 16-bit type can be modelled exactly.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -294,7 +302,10 @@ def attn_bwd(q, k, v, dout, cu_q, cu_kv, batch_size, mask_type=None,
                           where=has_key[:, None])
             dV = P.T @ dO
             dP = dO @ V.T
-            Drow = (P * dP).sum(axis=1)
+            if out is None:
+                Drow = (P * dP).sum(axis=1)
+            else:
+                Drow = (dO * np.asarray(out[oq:oq + lq, hq, :], dtype=np.float64)).sum(axis=1)
             dS = P * (dP - Drow[:, None])
             dq[oq:oq + lq, hq, :] += scale * (dS @ K)
             dk[ok:ok + lk, hk, :] += scale * (dS.T @ Q)
@@ -358,45 +369,96 @@ def attn_rows(q, k, v, dout, cu_q, cu_kv, b, hq, rows, mask_type=None,
 
 
 # ---------------------------------------------------------------------------
-# Context parallelism (Megatron-LM issue "How to pad sequences that cannot be
-# evenly split in context parallelism (CP)?", question): a sequence split over
-# n ranks is padded to a multiple of 2n.  Reading (not on the pages): the
-# load-balanced split into 2n equal chunks, rank r taking chunks r and 2n-1-r,
-# pads at the end of the sequence.
+# Key/value gradients of a key range of one long sequence, by query-row blocks
 # ---------------------------------------------------------------------------
-def cp_padded_length(length, n):
-    """Rows of the padded sequence: the least multiple of 2n that holds it."""
-    return -(-int(length) // (2 * n)) * (2 * n)
+
+def attn_bwd_key_range(q, k, v, dout, cu_q, cu_kv, b, hk, key_ranges, mask_type=None,
+                       cu_q_padded=None, cu_kv_padded=None, scale=None, row_block=1024):
+    """dK and dV of key ranges [lo, hi) of sequence b, kv head hk, summed over
+    the query heads of hk's GQA group (the ``attn_bwd`` definitions).
+
+    Key j's gradients are sums over query rows i: dV_j = sum_i P_ij dO_i and
+    dK_j = scale sum_i dS_ij Q_i, with dS_ij = P_ij (dP_ij - D_i).  P_ij and
+    D_i need the whole row i (its softmax normaliser and rowsum(P * dP)), so
+    the rows are taken in blocks of at most ``row_block``: each block's scores
+    against the keys its rows can see give its P and dP, and the block adds
+    its terms for the chosen keys.  This bounds memory for sequences of tens of
+    thousands of tokens.  Under a causal mask type no row of a block sees a
+    key past its last row's diagonal, so those keys (whose P is exactly 0) are
+    not formed.  ``key_ranges``: list of (lo, hi); returns a list of
+    (dk, dv), each [hi - lo, d].
+    """
+    T_q, h_q, d = q.shape
+    h_kv = k.shape[1]
+    group = h_q // h_kv
+    scale = _default_scale(d, scale)
+    (oq, lq), = [sequence_rows(cu_q, b + 1, cu_q_padded)[b]]
+    (ok, lk), = [sequence_rows(cu_kv, b + 1, cu_kv_padded)[b]]
+    for lo, hi in key_ranges:
+        if not 0 <= lo <= hi <= lk:
+            raise IndexError((lo, hi, lk))
+    mt = _mask_type(mask_type, b)
+    off = lk - lq if mt == MASK_CAUSAL_BOTTOM_RIGHT else 0
+    K = np.asarray(k[ok:ok + lk, hk, :], dtype=np.float64)
+    V = np.asarray(v[ok:ok + lk, hk, :], dtype=np.float64)
+    res = [(np.zeros((hi - lo, d)), np.zeros((hi - lo, d))) for lo, hi in key_ranges]
+    for hq in range(hk * group, (hk + 1) * group):
+        for r0 in range(0, lq, row_block):
+            r1 = min(r0 + row_block, lq)
+            # keys [0, n) can be visible to rows r0 .. r1-1
+            n = lk if mt not in (MASK_CAUSAL, MASK_CAUSAL_BOTTOM_RIGHT) else \
+                min(max(r1 + off, 0), lk)
+            Q = np.asarray(q[oq + r0:oq + r1, hq, :], dtype=np.float64)
+            dO = np.asarray(dout[oq + r0:oq + r1, hq, :], dtype=np.float64)
+            # rows r0 .. r1-1 of visible_keys(lq, lk, mt), keys 0 .. n-1
+            i = np.arange(r0, r1)[:, None]
+            j = np.arange(n)[None, :]
+            allowed = np.ones((r1 - r0, n), dtype=bool)
+            if mt == MASK_CAUSAL:
+                allowed &= j <= i
+            elif mt == MASK_CAUSAL_BOTTOM_RIGHT:
+                allowed &= j <= i + (lk - lq)
+            has_key = allowed.any(axis=1)
+            S = np.where(allowed, scale * (Q @ K[:n].T), -np.inf)
+            m = np.where(has_key, S.max(axis=1, initial=-np.inf), 0.0)
+            E = np.where(allowed, np.exp(S - m[:, None]), 0.0)
+            denom = E.sum(axis=1)
+            P = np.divide(E, denom[:, None], out=np.zeros_like(E), where=has_key[:, None])
+            dP = dO @ V[:n].T
+            Drow = (P * dP).sum(axis=1)
+            for (lo, hi), (dk, dv) in zip(key_ranges, res):
+                a, z = min(lo, n), min(hi, n)        # keys past n: P = 0, no term
+                if a == z:
+                    continue
+                Pr = P[:, a:z]
+                dS = Pr * (dP[:, a:z] - Drow[:, None])
+                dv[a - lo:z - lo] += Pr.T @ dO
+                dk[a - lo:z - lo] += scale * (dS.T @ Q)
+    return res
 
 
-def cp_local_positions(length, n, r):
-    """Positions (0 .. padded length - 1) of the padded sequence held by rank
-    r, in its local order: chunk r, then chunk 2n-1-r."""
-    padded = cp_padded_length(length, n)
-    c = padded // (2 * n)
-    chunks = [r, 2 * n - 1 - r]
-    return [k * c + i for k in chunks for i in range(c)]
+# ---------------------------------------------------------------------------
+# Rounding to the 16-bit storage types
+# ---------------------------------------------------------------------------
 
+def round_to_storage(x, dtype):
+    """x (any float array) rounded to nearest-even in "fp16" or "bf16" and
+    returned as float64: the values a 16-bit tensor of that type holds.
 
-def cp_attn_rank(q, k, v, lengths, n, r, mask_type=None, scale=None):
-    """Rank r's outputs by the definition: the full attention of every
-    sequence (``attn_fwd`` on the unsplit, unpadded sequences), read at the
-    positions rank r holds.  Returns (o [rows, h_q, d], lse [h_q, rows]) for
-    rank r's local rows, pad positions 0 / -inf.  q, k, v: [sum lengths, h, d]
-    packed without padding."""
-    lengths = [int(x) for x in lengths]
-    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
-    o_full, lse_full = attn_fwd(q, k, v, cu, cu, len(lengths), mask_type=mask_type, scale=scale)
-    rows_o, rows_l = [], []
-    for b, length in enumerate(lengths):
-        for pos in cp_local_positions(length, n, r):
-            if pos < length:
-                rows_o.append(o_full[cu[b] + pos])
-                rows_l.append(lse_full[:, cu[b] + pos])
-            else:
-                rows_o.append(np.zeros_like(o_full[0]))
-                rows_l.append(np.full(lse_full.shape[0], -np.inf))
-    h = q.shape[1]
-    if not rows_o:
-        return np.zeros((0, h, q.shape[2])), np.zeros((h, 0))
-    return np.stack(rows_o), np.stack(rows_l, axis=1)
+    fp16 is numpy's half.  bf16 keeps the upper 16 bits of the IEEE binary32
+    pattern: x is first rounded to binary32, then the lower 16 bits are
+    rounded away to nearest, ties to even (add 0x7FFF plus the lowest kept
+    bit, then truncate).  NaN is kept as a quiet NaN.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    if dtype == "fp16":
+        with np.errstate(over="ignore"):
+            return x.astype(np.float16).astype(np.float64)
+    if dtype != "bf16":
+        raise ValueError(dtype)
+    with np.errstate(over="ignore"):
+        f = x.astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000).astype(np.uint32)
+    out = r.view(np.float32).astype(np.float64)
+    return np.where(np.isnan(x), np.nan, out)

@@ -133,32 +133,6 @@ def test_workspace_size_and_check():
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, mis, need, None) == -4
 
 
-def test_one_pass_merge_and_sum_host_checks():
-    # argument errors are returned before anything is launched
-    lib = _lib.load()
-    vp = ctypes.c_void_p
-    lib.thd_attn_lse_merge_n.argtypes = [vp, vp, ctypes.c_int32, vp, vp, ctypes.c_int64,
-                                         ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, vp]
-    lib.thd_sum_n.argtypes = [vp, ctypes.c_int32, vp, ctypes.c_int64, ctypes.c_int32, vp]
-    parts = (vp * 9)(*([P] * 9))
-    merge = lambda n, **kw: lib.thd_attn_lse_merge_n(
-        kw.get("o", parts), kw.get("l", parts), n, kw.get("out", P), None, kw.get("total", 4),
-        kw.get("h", 2), kw.get("d", 64), kw.get("dtype", _lib.THD_BF16), None)
-    assert merge(0) == -2 and merge(9) == -2
-    assert merge(2, d=12) == -2 and merge(2, h=0) == -2 and merge(2, total=-1) == -2
-    assert merge(2, dtype=7) == -3
-    assert merge(2, out=None) == -1 and merge(2, o=None) == -1
-    assert merge(2, o=(vp * 2)(P, None)) == -1
-    assert merge(2, o=(vp * 2)(P, vp(0x2002))) == -3
-    assert merge(2, total=0) == 0
-    s = lambda n, **kw: lib.thd_sum_n(kw.get("x", parts), n, kw.get("out", P),
-                                      kw.get("count", 64), kw.get("dtype", _lib.THD_BF16), None)
-    assert s(0) == -2 and s(9) == -2 and s(2, count=12) == -2 and s(2, count=-8) == -2
-    assert s(2, dtype=7) == -3 and s(2, out=None) == -1 and s(2, x=(vp * 2)(None, P)) == -1
-    assert s(2, out=vp(0x2008)) == -3
-    assert s(2, count=0) == 0
-
-
 def test_padding_mask_host_checks():
     lib = _lib.load()
     assert lib.thd_padding_mask(P, -1, 4, P, None) == -2

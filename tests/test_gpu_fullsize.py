@@ -1,13 +1,17 @@
 """GPU: the synthetic configurations at full size, in the benchmark's launch
 configuration, checked against the oracle on samples it can compute quickly:
 output, LSE and dq of selected query rows (the oracle evaluates those rows
-alone), dk/dv of whole selected sequences, and every pad row bit-exact +0."""
+alone); dk/dv of the shortest sequence, the one with the most query rows and
+the one with the most keys -- whole when the oracle is cheap, else the first,
+a middle and the last 256-key tile over every query head of one kv head (the
+oracle takes such a key range by query-row blocks); and every pad row
+bit-exact +0."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from oracle import attn_bwd, attn_rows
+from oracle import attn_bwd, attn_bwd_key_range, attn_rows
 from gpu_helpers import assert_close, assert_pad_rows_zero, dev_meta, gpu_bwd, gpu_fwd
 
 pytestmark = pytest.mark.gpu
@@ -17,7 +21,13 @@ def seq_slice(t, start, n, head):
     return t[start:start + n, head:head + 1].to("cpu", torch.float64).numpy()
 
 
-def check_config(name, n_row_seqs=3, n_full_seqs=2, max_full_len=1200):
+# Sequences with at most this many (query, key) pairs get whole dk/dv from the
+# whole-sequence oracle; longer ones three 256-key tiles from the key-range one.
+WHOLE_PAIRS = 1 << 23
+TILE = 256
+
+
+def check_config(name, n_row_seqs=3):
     w = workloads.config(name)
     print(f"config {name}: B={w.batch} Tq={w.T_q} Tkv={w.T_kv} h={w.h_q}/{w.h_kv}", flush=True)
     q, k, v, do = workloads.make_tensors(w, device="cuda")
@@ -59,24 +69,42 @@ def check_config(name, n_row_seqs=3, n_full_seqs=2, max_full_len=1200):
             assert np.abs(gl - rl).max() < 1e-3
     assert_close(f"cfg{name} out rows", np.concatenate(got_o), np.concatenate(ref_o), w.dtype)
     assert_close(f"cfg{name} dq rows", np.concatenate(got_dq), np.concatenate(ref_dq), w.dtype)
-    # --- whole sequences: dk, dv (all query heads of one kv head) ----------
-    cand = [int(b) for b in order if 0 < w.lens_q[b] <= max_full_len and w.lens_kv[b] > 0]
-    full_seqs = cand[:1] + cand[-1:] if len(cand) > 1 else cand
-    for b in full_seqs[:n_full_seqs]:
+    # --- dk, dv of chosen sequences (all query heads of one kv head) ----------
+    have = [int(b) for b in range(w.batch) if w.lens_q[b] > 0 and w.lens_kv[b] > 0]
+    chosen = sorted({min(have, key=lambda b: (w.lens_q[b], b)),
+                     max(have, key=lambda b: (w.lens_q[b], -b)),
+                     max(have, key=lambda b: (w.lens_kv[b], -b))})
+    for b in chosen:
         lq, lk = int(w.lens_q[b]), int(w.lens_kv[b])
         hk = int(rng.integers(0, w.h_kv))
         heads = list(range(hk * group, (hk + 1) * group))
-        Q = q[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
-        G = do[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
-        K = seq_slice(k, sk[b], lk, hk)
-        V = seq_slice(v, sk[b], lk, hk)
-        cu_q = np.array([0, lq], np.int32)
-        cu_k = np.array([0, lk], np.int32)
-        _, rdk, rdv = attn_bwd(Q, K, V, G, cu_q, cu_k, 1, [w.causal[b]])
-        assert_close(f"cfg{name} dk seq{b}", dk[sk[b]:sk[b] + lk, hk].cpu().double().numpy(),
-                     rdk[:, 0], w.dtype)
-        assert_close(f"cfg{name} dv seq{b}", dv[sk[b]:sk[b] + lk, hk].cpu().double().numpy(),
-                     rdv[:, 0], w.dtype)
+        got_k = dk[sk[b]:sk[b] + lk, hk].cpu().double().numpy()
+        got_v = dv[sk[b]:sk[b] + lk, hk].cpu().double().numpy()
+        if lq * lk <= WHOLE_PAIRS:
+            Q = q[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
+            G = do[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
+            K = seq_slice(k, sk[b], lk, hk)
+            V = seq_slice(v, sk[b], lk, hk)
+            cu_q = np.array([0, lq], np.int32)
+            cu_k = np.array([0, lk], np.int32)
+            _, rdk, rdv = attn_bwd(Q, K, V, G, cu_q, cu_k, 1, [w.causal[b]])
+            ranges, refs = [(0, lk)], [(rdk[:, 0], rdv[:, 0])]
+        else:
+            n_t = (lk + TILE - 1) // TILE
+            ranges = [(t * TILE, min((t + 1) * TILE, lk)) for t in sorted({0, n_t // 2, n_t - 1})]
+            # one kv head and its query heads, as a sequence of their own
+            Q = q[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
+            G = do[sq[b]:sq[b] + lq, heads].to("cpu", torch.float64).numpy()
+            K = seq_slice(k, sk[b], lk, hk)
+            V = seq_slice(v, sk[b], lk, hk)
+            cu_q = np.array([0, lq], np.int32)
+            cu_k = np.array([0, lk], np.int32)
+            refs = attn_bwd_key_range(Q, K, V, G, cu_q, cu_k, 0, 0, ranges, [w.causal[b]])
+        for (lo, hi), (rk, rv) in zip(ranges, refs):
+            print(f"config {name}: dk/dv seq {b} (lq={lq}, lk={lk}) keys [{lo},{hi}) "
+                  f"kv head {hk}", flush=True)
+            assert_close(f"cfg{name} dk seq{b} [{lo},{hi})", got_k[lo:hi], rk, w.dtype)
+            assert_close(f"cfg{name} dv seq{b} [{lo},{hi})", got_v[lo:hi], rv, w.dtype)
     print(f"config {name}: ok", flush=True)
 
 

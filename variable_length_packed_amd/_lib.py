@@ -31,12 +31,6 @@ EXPORTED = (
     "thd_attn_bwd_workspace_size",
     "thd_attn_bwd",
     "thd_attn_bwd_timed",
-    "thd_cp_layout",
-    "thd_cp_gather",
-    "thd_attn_lse_merge",
-    "thd_accumulate",
-    "thd_attn_lse_merge_n",
-    "thd_sum_n",
     "thd_status_string",
     "thd_version",
 )

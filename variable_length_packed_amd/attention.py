@@ -9,8 +9,6 @@ properties (device, dtype, shape, contiguity), allocate outputs with torch and
 pass raw pointers plus the current HIP stream to libthdattn.so; they never read
 device data, so no call synchronises with the host.
 """
-import math
-
 import torch
 
 from . import _lib
@@ -33,15 +31,33 @@ def _ptr(t):
     return ctypes_void(t.data_ptr()) if t is not None and t.numel() > 0 else None
 
 
-def _require_cuda(name, t, dtype=None):
+# Device type every tensor argument must live on (the library's kernels run
+# on the GPU; the host-side checks below are exercised on the CPU by
+# replacing this with "cpu").
+_DEVICE_TYPE = "cuda"
+
+
+def _require_cuda(name, t, dtype=None, shape=None, device=None):
+    """Host-visible checks of one tensor argument: type, device, dtype, shape,
+    contiguity.  Raises before anything is launched."""
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if t.device.type != _DEVICE_TYPE:
         raise ValueError(f"{name} must be on a GPU device (got {t.device})")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+def _require_workspace(workspace, need, device):
+    _require_cuda("workspace", workspace, torch.uint8, device=device)
+    if workspace.numel() < need:
+        raise ValueError(f"workspace holds {workspace.numel()} bytes, {need} needed")
 
 
 def padding_mask(cu_seqlens, batch_size, max_seqlen):
@@ -69,7 +85,7 @@ def padding_mask(cu_seqlens, batch_size, max_seqlen):
 def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
                softmax_scale, batch_size):
     _require_cuda("q", q, tuple(_DTYPES))
-    _require_cuda("k", k, q.dtype)
+    _require_cuda("k", k, q.dtype, device=q.device)
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("q and k must be [T, h, d]")
     if q.shape[2] != k.shape[2]:
@@ -77,7 +93,7 @@ def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
     for name, t in (("cu_seqlens_q", cu_q), ("cu_seqlens_kv", cu_kv),
                     ("cu_seqlens_q_padded", cu_q_pad), ("cu_seqlens_kv_padded", cu_kv_pad)):
         if t is not None:
-            _require_cuda(name, t, torch.int32)
+            _require_cuda(name, t, torch.int32, device=q.device)
     if batch_size is None:
         batch_size = cu_q.numel() - 1
     batch_size = int(batch_size)
@@ -88,7 +104,7 @@ def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,
         if t is not None and t.numel() < batch_size + (0 if "padded" in name else 1):
             raise ValueError(f"{name} is shorter than the batch")
     if is_causal is not None:
-        _require_cuda("mask_type", is_causal, (torch.bool, torch.uint8))
+        _require_cuda("mask_type", is_causal, (torch.bool, torch.uint8), device=q.device)
         if is_causal.numel() < batch_size:
             raise ValueError("mask_type / is_causal needs one entry per sequence")
     a = _lib.ThdVarlenArgs()
@@ -136,22 +152,18 @@ def attn_fwd(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv, 
     a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                    cu_seqlens_q_padded, cu_seqlens_kv_padded, is_causal, softmax_scale,
                    batch_size)
-    _require_cuda("v", v, q.dtype)
-    if v.shape != k.shape:
-        raise ValueError("v must have the shape of k")
+    _require_cuda("v", v, q.dtype, shape=k.shape, device=q.device)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
         lse = torch.empty((q.shape[1], q.shape[0]), dtype=torch.float32, device=q.device)
-    _require_cuda("out", out, q.dtype)
-    _require_cuda("lse", lse, torch.float32)
-    if out.shape != q.shape or lse.shape != (q.shape[1], q.shape[0]):
-        raise ValueError("out / lse have the wrong shape")
+    _require_cuda("out", out, q.dtype, shape=q.shape, device=q.device)
+    _require_cuda("lse", lse, torch.float32, shape=(q.shape[1], q.shape[0]), device=q.device)
     lib = _lib.load()
     need = int(lib.thd_attn_fwd_workspace_size(a))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _require_cuda("workspace", workspace, torch.uint8)
+    _require_workspace(workspace, need, q.device)
     st = lib.thd_attn_fwd(a, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), _ptr(workspace),
                           workspace.numel(), _stream(q.device))
     _lib.check(st, "thd_attn_fwd")
@@ -176,27 +188,30 @@ def attn_bwd(q, k, v, out, dout, lse, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q,
              max_seqlen_kv, *, cu_seqlens_q_padded=None, cu_seqlens_kv_padded=None,
              is_causal=None, softmax_scale=None, batch_size=None, workspace=None,
              dq=None, dk=None, dv=None, mask_type=None):
-    """Backward attention; returns (dq, dk, dv).  Arguments as ``attn_fwd``."""
+    """Backward attention; returns (dq, dk, dv).  Arguments as ``attn_fwd``;
+    ``dq``, ``dk``, ``dv`` (optional outputs) must have the dtype, shape and
+    device of q, k, v.  Every tensor is checked before anything is launched."""
     is_causal = _mask_arg(is_causal, mask_type)
     a = _make_args(q, k, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen_kv,
                    cu_seqlens_q_padded, cu_seqlens_kv_padded, is_causal, softmax_scale,
                    batch_size)
+    dev = q.device
     for name, t, like in (("v", v, k), ("out", out, q), ("dout", dout, q)):
-        _require_cuda(name, t, q.dtype)
-        if t.shape != like.shape:
-            raise ValueError(f"{name} has the wrong shape")
-    _require_cuda("lse", lse, torch.float32)
-    lib = _lib.load()
-    need = int(lib.thd_attn_bwd_workspace_size(a))
-    if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    _require_cuda("workspace", workspace, torch.uint8)
+        _require_cuda(name, t, q.dtype, shape=like.shape, device=dev)
+    _require_cuda("lse", lse, torch.float32, shape=(q.shape[1], q.shape[0]), device=dev)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
+    for name, t, like in (("dq", dq, q), ("dk", dk, k), ("dv", dv, v)):
+        _require_cuda(name, t, q.dtype, shape=like.shape, device=dev)
+    lib = _lib.load()
+    need = int(lib.thd_attn_bwd_workspace_size(a))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _require_workspace(workspace, need, dev)
     st = lib.thd_attn_bwd(a, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse),
                           _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(),
-                          _stream(q.device))
+                          _stream(dev))
     _lib.check(st, "thd_attn_bwd")
     return dq, dk, dv
 
@@ -234,7 +249,3 @@ def thd_attention(q, k, v, cu_seqlens_q, cu_seqlens_kv, max_seqlen_q, max_seqlen
 MASK_PADDING = 0
 MASK_CAUSAL = 1
 MASK_CAUSAL_BOTTOM_RIGHT = 2
-
-
-def default_scale(head_dim):
-    return 1.0 / math.sqrt(head_dim)

@@ -176,113 +176,4 @@ int thd_attn_bwd_timed(const thd_varlen_args* args, const void* q, const void* k
                        stream, events);
 }
 
-int thd_cp_layout(const int32_t* cu_seqlens, const uint8_t* mask_type, int32_t batch,
-                  int32_t cp_size, int32_t rank, int32_t peer, int32_t side,
-                  int32_t* out_cu_seqlens, int32_t* out_cu_seqlens_padded,
-                  int32_t* out_global_cu_seqlens_padded, uint8_t* out_mask_type, void* stream) {
-  if (batch < 0 || cp_size < 1 || rank < 0 || rank >= cp_size || peer < 0 || peer >= cp_size ||
-      (side != 0 && side != 1))
-    return THD_ERR_SHAPE;
-  if (!cu_seqlens) return THD_ERR_NULL;
-  thd::CpLayoutArgs a{cu_seqlens, mask_type, batch, cp_size, rank, peer, side,
-                      out_cu_seqlens, out_cu_seqlens_padded, out_global_cu_seqlens_padded,
-                      out_mask_type};
-  return thd::launch_cp_layout(a, (hipStream_t)stream) == hipSuccess ? THD_OK : THD_ERR_HIP;
-}
-
-int thd_cp_gather(const int32_t* cu_seqlens, const int32_t* local_cu_seqlens_padded,
-                  const int32_t* global_cu_seqlens_padded, int32_t batch, int32_t cp_size,
-                  int32_t rank, const void* src, int64_t total_global, void* dst,
-                  int64_t total_local, int32_t row_bytes, void* stream) {
-  if (batch < 0 || cp_size < 1 || rank < 0 || rank >= cp_size || total_global < 0 ||
-      total_local < 0 || row_bytes <= 0 || row_bytes % 16 != 0)
-    return THD_ERR_SHAPE;
-  if (batch == 0 || total_local == 0) return THD_OK;
-  if (!cu_seqlens || !local_cu_seqlens_padded || !global_cu_seqlens_padded || !dst ||
-      (total_global > 0 && !src))
-    return THD_ERR_NULL;
-  if (!aligned16(dst) || (src && !aligned16(src))) return THD_ERR_UNSUPPORTED;
-  thd::CpGatherArgs a{cu_seqlens, local_cu_seqlens_padded, global_cu_seqlens_padded, batch,
-                      cp_size, rank, src, total_global, dst, total_local, row_bytes};
-  return thd::launch_cp_gather(a, (hipStream_t)stream) == hipSuccess ? THD_OK : THD_ERR_HIP;
-}
-
-int thd_attn_lse_merge(const void* o_part, const float* lse_part, float* o_acc, float* lse_acc,
-                       void* o_out, int64_t total, int32_t h, int32_t head_dim, int32_t dtype,
-                       int32_t first, void* stream) {
-  if (total < 0 || h <= 0 || head_dim <= 0 || head_dim % 8 != 0) return THD_ERR_SHAPE;
-  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
-  if (total == 0) return THD_OK;
-  if (!o_part || !lse_part || !o_acc || !lse_acc) return THD_ERR_NULL;
-  if (!aligned16(o_part) || !aligned16(o_acc) || (o_out && !aligned16(o_out)))
-    return THD_ERR_UNSUPPORTED;
-  thd::MergeArgs a{o_part, lse_part, o_acc, lse_acc, o_out, total, h, head_dim, first != 0};
-  return thd::launch_lse_merge(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
-             ? THD_OK
-             : THD_ERR_HIP;
-}
-
-int thd_accumulate(const void* src, float* acc, void* out, int64_t n_elems, int32_t dtype,
-                   int32_t first, void* stream) {
-  if (n_elems < 0 || n_elems % 8 != 0) return THD_ERR_SHAPE;
-  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
-  if (n_elems == 0) return THD_OK;
-  if (!src || !acc) return THD_ERR_NULL;
-  if (!aligned16(src) || !aligned16(acc) || (out && !aligned16(out))) return THD_ERR_UNSUPPORTED;
-  thd::AccumulateArgs a{src, acc, out, n_elems, first != 0};
-  return thd::launch_accumulate(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
-             ? THD_OK
-             : THD_ERR_HIP;
-}
-
-int thd_attn_lse_merge_n(const void* const* o_parts, const float* const* lse_parts,
-                         int32_t n_parts, void* o_out, float* lse_out, int64_t total, int32_t h,
-                         int32_t head_dim, int32_t dtype, void* stream) {
-  if (total < 0 || h <= 0 || head_dim <= 0 || head_dim % 8 != 0 || n_parts < 1 ||
-      n_parts > thd::kMaxParts)
-    return THD_ERR_SHAPE;
-  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
-  if (total == 0) return THD_OK;
-  if (!o_parts || !lse_parts || !o_out) return THD_ERR_NULL;
-  thd::MergeNArgs a = {};
-  for (int k = 0; k < n_parts; ++k) {
-    if (!o_parts[k] || !lse_parts[k]) return THD_ERR_NULL;
-    if (!aligned16(o_parts[k])) return THD_ERR_UNSUPPORTED;
-    a.o[k] = o_parts[k];
-    a.lse[k] = lse_parts[k];
-  }
-  if (!aligned16(o_out)) return THD_ERR_UNSUPPORTED;
-  a.n = n_parts;
-  a.o_out = o_out;
-  a.lse_out = lse_out;
-  a.total = total;
-  a.h = h;
-  a.d = head_dim;
-  return thd::launch_lse_merge_n(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
-             ? THD_OK
-             : THD_ERR_HIP;
-}
-
-int thd_sum_n(const void* const* parts, int32_t n_parts, void* out, int64_t n_elems,
-              int32_t dtype, void* stream) {
-  if (n_elems < 0 || n_elems % 8 != 0 || n_parts < 1 || n_parts > thd::kMaxParts)
-    return THD_ERR_SHAPE;
-  if (dtype != THD_FP16 && dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
-  if (n_elems == 0) return THD_OK;
-  if (!parts || !out) return THD_ERR_NULL;
-  thd::SumNArgs a = {};
-  for (int k = 0; k < n_parts; ++k) {
-    if (!parts[k]) return THD_ERR_NULL;
-    if (!aligned16(parts[k])) return THD_ERR_UNSUPPORTED;
-    a.x[k] = parts[k];
-  }
-  if (!aligned16(out)) return THD_ERR_UNSUPPORTED;
-  a.n = n_parts;
-  a.out = out;
-  a.count = n_elems;
-  return thd::launch_sum_n(a, dtype == THD_BF16, (hipStream_t)stream) == hipSuccess
-             ? THD_OK
-             : THD_ERR_HIP;
-}
-
 }  // extern "C"
