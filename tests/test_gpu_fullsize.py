@@ -108,6 +108,7 @@ def check_config(name, n_row_seqs=3):
     print(f"config {name}: ok", flush=True)
 
 
+@pytest.mark.timeout(400)   # the long-sequence oracle tiles take tens of seconds on the host
 @pytest.mark.parametrize("name", ["2", "3", "5", "4", "6", "7"])
 def test_full_size_config(name):
     check_config(name)
