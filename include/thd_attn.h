@@ -140,6 +140,26 @@ int thd_attn_fwd(const thd_varlen_args* args, const void* q, const void* k,
                  const void* v, void* o, float* lse, void* workspace,
                  size_t workspace_bytes, void* stream);
 
+/* Largest forward workspace (bytes) thd_attn_fwd_noalloc can provide. */
+#define THD_FWD_NOALLOC_MAX_WORKSPACE (16u << 20)
+
+/* thd_attn_fwd for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same validation, kernels and results as thd_attn_fwd, with the
+ * workspace taken from a fixed device array of THD_FWD_NOALLOC_MAX_WORKSPACE
+ * bytes inside the library (one per device, held until the process ends)
+ * instead of a caller buffer.  The caller still passes every input and
+ * output.  The call allocates and frees nothing; its first call on a device
+ * looks up that device's array (call it once before a graph capture), with
+ * the stream's device current.  Every call on one device shares that
+ * device's array, and nothing in it needs to start at zero; calls that
+ * overlap in time on one device (several streams or host threads) race on it
+ * and their results are undefined.  Errors: as thd_attn_fwd, and
+ * THD_ERR_WORKSPACE when thd_attn_fwd_workspace_size(args) exceeds
+ * THD_FWD_NOALLOC_MAX_WORKSPACE (returned before anything is launched). */
+int thd_attn_fwd_noalloc(const thd_varlen_args* args, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* stream);
+
 /* Bytes of device workspace thd_attn_bwd needs for these arguments (an fp32
  * dq accumulator and per-row fp32 statistics), 0 if the arguments are
  * invalid.  The workspace needs no initialisation. */

@@ -119,6 +119,21 @@ def test_fwd_workspace_size_and_check():
     assert lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, mis, need, None) == -4
 
 
+def test_noalloc_forward_host_checks():
+    # the forward that allocates nothing rejects, before any launch, a problem
+    # whose workspace exceeds its fixed device array, and validates like the
+    # forward
+    lib = _lib.load()
+    big = _args(batch=1, max_seqlen_q=64, max_seqlen_kv=64, total_q=300_000_000,
+                total_kv=16, h_q=1, h_kv=1, head_dim=8)
+    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(big)) > _lib.FWD_NOALLOC_MAX_WORKSPACE
+    assert lib.thd_attn_fwd_noalloc(ctypes.byref(big), P, P, P, P, P, None) == -4
+    assert lib.thd_attn_fwd_noalloc(ctypes.byref(_args(batch=-1)), P, P, P, P, P, None) == -2
+    assert lib.thd_attn_fwd_noalloc(ctypes.byref(_args(head_dim=12)), P, P, P, P, P, None) == -3
+    assert lib.thd_attn_fwd_noalloc(ctypes.byref(_args()), None, P, P, P, P, None) == -1
+    assert lib.thd_attn_fwd_noalloc(None, P, P, P, P, P, None) == -1
+
+
 def test_workspace_size_and_check():
     lib = _lib.load()
     a = _args()

@@ -14,6 +14,9 @@ LIB_PATH = os.path.join(PKG_DIR, "libthdattn.so")
 THD_FP16 = 0
 THD_BF16 = 1
 
+# THD_FWD_NOALLOC_MAX_WORKSPACE of include/thd_attn.h
+FWD_NOALLOC_MAX_WORKSPACE = 16 << 20
+
 STATUS = {
     0: "THD_OK",
     -1: "THD_ERR_NULL",
@@ -28,6 +31,7 @@ EXPORTED = (
     "thd_padding_mask",
     "thd_attn_fwd_workspace_size",
     "thd_attn_fwd",
+    "thd_attn_fwd_noalloc",
     "thd_attn_bwd_workspace_size",
     "thd_attn_bwd",
     "thd_attn_bwd_timed",
@@ -85,6 +89,8 @@ def load(path=None):
     lib.thd_attn_fwd_workspace_size.restype = sz
     lib.thd_attn_fwd.argtypes = [argsp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.thd_attn_fwd.restype = ctypes.c_int
+    lib.thd_attn_fwd_noalloc.argtypes = [argsp, vp, vp, vp, vp, vp, vp]
+    lib.thd_attn_fwd_noalloc.restype = ctypes.c_int
     lib.thd_attn_bwd_workspace_size.argtypes = [argsp]
     lib.thd_attn_bwd_workspace_size.restype = sz
     lib.thd_attn_bwd.argtypes = [argsp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]

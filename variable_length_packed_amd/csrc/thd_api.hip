@@ -8,6 +8,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "thd_attn.h"
 #include "thd_launch.hpp"
 
@@ -77,6 +79,51 @@ int check_tensor(const void* ptr, int64_t rows) {
   return THD_OK;
 }
 
+// Host-visible checks of a forward call: the problem plus its tensors.
+int fwd_problem(const thd_varlen_args* args, const void* q, const void* k, const void* v,
+                const void* o, const float* lse, thd::Problem* p) {
+  int st = to_problem(args, p, false);
+  if (st != THD_OK) return st;
+  const int64_t Tq = p->T_q, Tk = p->T_kv;
+  if ((st = check_tensor(q, Tq)) || (st = check_tensor(o, Tq)) || (st = check_tensor(k, Tk)) ||
+      (st = check_tensor(v, Tk)))
+    return st;
+  if (Tq > 0 && !lse) return THD_ERR_NULL;
+  return THD_OK;
+}
+
+// The forward's workspace for callers that cannot allocate
+// (thd_attn_fwd_noalloc): a fixed array in device memory, one copy per
+// device, held until the process ends.
+constexpr size_t kNoAllocScratchBytes = (size_t)THD_FWD_NOALLOC_MAX_WORKSPACE;
+constexpr int kMaxDevices = 256;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, looked up once
+// per device with that device current.  On the host the array's name is
+// only a stand-in for the symbol, never a device address: kernels and copies
+// get this pointer instead.
+int scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return THD_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return THD_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return THD_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -89,7 +136,7 @@ const char* thd_status_string(int status) {
     case THD_ERR_NULL: return "THD_ERR_NULL: a required pointer is NULL";
     case THD_ERR_SHAPE: return "THD_ERR_SHAPE: a size is negative or inconsistent";
     case THD_ERR_UNSUPPORTED: return "THD_ERR_UNSUPPORTED: head_dim, dtype or alignment not supported";
-    case THD_ERR_WORKSPACE: return "THD_ERR_WORKSPACE: backward workspace missing or too small";
+    case THD_ERR_WORKSPACE: return "THD_ERR_WORKSPACE: workspace missing, too small or misaligned";
     case THD_ERR_HIP: return "THD_ERR_HIP: the HIP runtime refused a launch";
     default: return "unknown thd_status";
   }
@@ -114,19 +161,27 @@ size_t thd_attn_fwd_workspace_size(const thd_varlen_args* args) {
 int thd_attn_fwd(const thd_varlen_args* args, const void* q, const void* k, const void* v,
                  void* o, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   thd::Problem p;
-  int st = to_problem(args, &p, false);
+  int st = fwd_problem(args, q, k, v, o, lse, &p);
   if (st != THD_OK) return st;
-  const int64_t Tq = p.T_q, Tk = p.T_kv;
-  if ((st = check_tensor(q, Tq)) || (st = check_tensor(o, Tq)) || (st = check_tensor(k, Tk)) ||
-      (st = check_tensor(v, Tk)))
-    return st;
-  if (Tq > 0 && !lse) return THD_ERR_NULL;
   const size_t need = thd::fwd_workspace_bytes(p);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return THD_ERR_WORKSPACE;
     if (((uintptr_t)workspace & 255u) != 0) return THD_ERR_WORKSPACE;
   }
   hipError_t e = thd::launch_fwd(p, q, k, v, o, lse, workspace, (hipStream_t)stream);
+  return e == hipSuccess ? THD_OK : THD_ERR_HIP;
+}
+
+int thd_attn_fwd_noalloc(const thd_varlen_args* args, const void* q, const void* k,
+                         const void* v, void* o, float* lse, void* stream) {
+  thd::Problem p;
+  int st = fwd_problem(args, q, k, v, o, lse, &p);
+  if (st != THD_OK) return st;
+  const size_t need = thd::fwd_workspace_bytes(p);
+  if (need > kNoAllocScratchBytes) return THD_ERR_WORKSPACE;
+  void* ws = nullptr;
+  if (need > 0 && (st = scratch_of_current_device(&ws)) != THD_OK) return st;
+  hipError_t e = thd::launch_fwd(p, q, k, v, o, lse, ws, (hipStream_t)stream);
   return e == hipSuccess ? THD_OK : THD_ERR_HIP;
 }
 
