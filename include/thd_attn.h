@@ -36,7 +36,7 @@
  *     max_seqlen_q * h_q * head_dim * 2 and max_seqlen_kv * h_kv * head_dim * 2
  *     must be below 2^31, and for the backward also
  *     max_seqlen_q * h_q * DP * 4 (its fp32 dq accumulator; DP = head_dim
- *     rounded up to 32, 64 or 128) and total_q * h_q / 32.  max_seqlen_* must
+ *     rounded up to 32, 64, 128 or 256) and total_q * h_q / 32.  max_seqlen_* must
  *     bound the true lengths: a longer sequence is clamped as above.
  *   - No C++ exception crosses this interface.
  *
@@ -105,7 +105,7 @@ typedef struct {
   int64_t total_kv;                    /* rows of k / v / dk / dv                  */
   int32_t h_q;                         /* query heads, >= 1                        */
   int32_t h_kv;                        /* key/value heads, h_q % h_kv == 0         */
-  int32_t head_dim;                    /* multiple of 8, 8..128                    */
+  int32_t head_dim;                    /* multiple of 8, 8..256                    */
   float softmax_scale;                 /* <= 0 or NaN => 1/sqrt(head_dim)          */
   int32_t dtype;                       /* thd_dtype of q/k/v/o/dout/dq/dk/dv       */
 } thd_varlen_args;

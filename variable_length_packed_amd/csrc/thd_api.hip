@@ -23,11 +23,11 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 // row, so max_seqlen rows of every buffer they address per sequence must
 // stay below 2^31 bytes: q / o rows (h_q * head_dim * 2 bytes), k / v rows
 // (h_kv * head_dim * 2) and, in the backward, the fp32 dq accumulator rows
-// (h_q * DP * 4, DP = head_dim rounded up to 32, 64 or 128).  The backward's
+// (h_q * DP * 4, DP = head_dim rounded up to 32, 64, 128 or 256).  The backward's
 // pre and post passes take one workgroup per 32 (row, head) pairs.
 int check_sizes(const thd_varlen_args* a, bool backward) {
   const int64_t lim = (int64_t)1 << 31;
-  const int dp = a->head_dim <= 32 ? 32 : a->head_dim <= 64 ? 64 : 128;
+  const int dp = a->head_dim <= 32 ? 32 : a->head_dim <= 64 ? 64 : a->head_dim <= 128 ? 128 : 256;
   const int64_t q_row = (int64_t)a->h_q * (backward ? dp * 4 : a->head_dim * 2);
   const int64_t kv_row = (int64_t)a->h_kv * a->head_dim * 2;
   if ((int64_t)a->max_seqlen_q * q_row >= lim || (int64_t)a->max_seqlen_kv * kv_row >= lim)
@@ -44,7 +44,7 @@ int to_problem(const thd_varlen_args* a, thd::Problem* p, bool backward) {
   if (a->h_q <= 0 || a->h_kv <= 0 || a->h_q % a->h_kv != 0) return THD_ERR_SHAPE;
   if (a->total_q >= kMaxRows || a->total_kv >= kMaxRows) return THD_ERR_SHAPE;
   if (a->dtype != THD_FP16 && a->dtype != THD_BF16) return THD_ERR_UNSUPPORTED;
-  if (a->head_dim < 8 || a->head_dim > 128 || a->head_dim % 8 != 0) return THD_ERR_UNSUPPORTED;
+  if (a->head_dim < 8 || a->head_dim > 256 || a->head_dim % 8 != 0) return THD_ERR_UNSUPPORTED;
   if (a->batch > 0 && (!a->cu_seqlens_q || !a->cu_seqlens_kv)) return THD_ERR_NULL;
   // grid bounds: query/key tiles times heads must fit a 32-bit grid
   const int64_t tiles_q = (a->total_q + 127) / 128 + a->batch;

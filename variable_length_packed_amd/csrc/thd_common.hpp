@@ -103,10 +103,11 @@ __device__ __forceinline__ float wave_sum_halves(float x) {
   return a + b;
 }
 
-// Sum of x over each aligned group of N lanes (N = 4, 8 or 16), in every
+// Sum of x over each aligned group of N lanes (N = 4, 8, 16 or 32), in every
 // lane of the group, by DPP row operations (no LDS round trip): exchanges
 // within pairs and within quads (quad permutes [1,0,3,2] and [2,3,0,1]), then
-// with the mirrored lane of the half row (8 lanes) and of the row (16 lanes).
+// with the mirrored lane of the half row (8 lanes) and of the row (16 lanes);
+// groups of 32 add the other row's sum with one lane shuffle.
 // Each step adds two partial sums in either order, so all lanes of a group
 // end with the same value.  Every lane of the wave must be active.
 template <int CTRL>
@@ -116,11 +117,12 @@ __device__ __forceinline__ float add_dpp(float v) {
 }
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
-  static_assert(N == 4 || N == 8 || N == 16, "DPP rows hold 16 lanes");
+  static_assert(N == 4 || N == 8 || N == 16 || N == 32, "groups of 4 to 32 lanes");
   x = add_dpp<0xB1>(x);                   // quad_perm [1,0,3,2]
   x = add_dpp<0x4E>(x);                   // quad_perm [2,3,0,1]
   if constexpr (N >= 8) x = add_dpp<0x141>(x);   // row_half_mirror
   if constexpr (N >= 16) x = add_dpp<0x140>(x);  // row_mirror
+  if constexpr (N >= 32) x += __shfl_xor(x, 16, 64);  // the neighbouring DPP row
   return x;
 }
 
@@ -230,7 +232,7 @@ __device__ __forceinline__ u32x2 lds_read_tr(const unsigned char* lds, uint32_t 
 // 16kb + 8 + 4h + {0..3} (j = 1).  With R = 4h + (g16 >> 2) < 8,
 //   swz(R + 16kb + 8j, C + 32dt) = swz(R, C) ^ tr_xor(dt, kb, j):
 // the row offset is a multiple of 8 added to R < 8, f sees only its bit 3
-// (as chunk bit 3, kept when DP = 128), and 4dt lies above C's chunk bits.
+// (as chunk bit 3, kept when DP >= 128), and 4dt lies above C's chunk bits.
 // The row part only sets row bits that are zero in swz(R, C), so it may also
 // be added (and then ride in an instruction's offset field).
 template <int DP>
@@ -239,7 +241,7 @@ __device__ __forceinline__ uint32_t tr_row(int kb, int j) {
 }
 template <int DP>
 __device__ __forceinline__ uint32_t tr_chunk(int dt, int j) {
-  return (uint32_t)(4 * dt ^ (DP == 128 ? 8 * j : 0)) << 4;
+  return (uint32_t)(4 * dt ^ (DP >= 128 ? 8 * j : 0)) << 4;
 }
 template <int DP>
 __device__ __forceinline__ uint32_t tr_xor(int dt, int kb, int j) {

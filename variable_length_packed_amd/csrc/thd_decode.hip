@@ -314,7 +314,9 @@ hipError_t launch_decode_t(const DecParams& dp, hipStream_t s) {
 
 bool decode_applies(const Problem& p) {
   const int group = p.h_q / p.h_kv;
-  if (!(p.batch > 0 && p.max_q >= 1 && (int64_t)p.max_q * group <= kDecRows && p.max_kv > 0))
+  // head dims above 128 take the tiled forward
+  if (!(p.batch > 0 && p.max_q >= 1 && (int64_t)p.max_q * group <= kDecRows && p.max_kv > 0 &&
+        p.d <= 128))
     return false;
   const DecodeShape ds = decode_shape(p);
   const int64_t wgs = (int64_t)p.batch * p.h_kv * ds.n_split;

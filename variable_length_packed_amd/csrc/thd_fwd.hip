@@ -36,11 +36,15 @@ constexpr int kFwdBM = 128;  // query rows per workgroup
 // (48 KB) on short and long causal sequences alike, and 64-key tiles in two
 // stages (two workgroups per CU) about 4.5 % slower; d = 64 keeps three
 // stages.  At d <= 32 a 32-key tile would be smaller than one 1 KB load per
-// wave, and 64-key tiles in two stages are kept.
+// wave, and 64-key tiles in two stages are kept.  Head dims above 128 (DP =
+// 256) take 32-key tiles in two stages (64 KB per workgroup) and two
+// workgroups per CU: their Q operand and accumulators need about 230
+// registers per lane.
 template <int DP>
 struct FwdTile {
   static constexpr int BN = DP > 32 ? 32 : 64;
-  static constexpr int NS = DP == 128 ? 2 : DP > 32 ? 3 : 2;
+  static constexpr int NS = DP >= 128 ? 2 : DP > 32 ? 3 : 2;
+  static constexpr int WG_PER_CU = DP > 128 ? 2 : DP > 32 ? 3 : 2;
 };
 constexpr int kWaveM = 32;   // query rows per wave
 constexpr int kZeroRows = 64;
@@ -139,7 +143,7 @@ __global__ __launch_bounds__(256) void thd_fwd_pre_kernel(FwdParams p) {
 constexpr float kRescaleLog2 = 8.0f;
 
 template <class DT, int DP>
-__global__ __launch_bounds__(256, DP > 32 ? 3 : 2) void thd_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, FwdTile<DP>::WG_PER_CU) void thd_fwd_kernel(FwdParams p) {
   constexpr int BM = kFwdBM, BN = FwdTile<DP>::BN, NS = FwdTile<DP>::NS;
   constexpr int NT = BN / 32;      // 32-key S^T tiles per LDS tile
   constexpr int NKB = BN / 16;     // 16-key blocks (MFMA K steps of O^T)
@@ -464,7 +468,9 @@ hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void
     return p.bf16 ? launch_fwd_t<Bf16, 32>(fp, n_pre, s) : launch_fwd_t<Fp16, 32>(fp, n_pre, s);
   if (p.d <= 64)
     return p.bf16 ? launch_fwd_t<Bf16, 64>(fp, n_pre, s) : launch_fwd_t<Fp16, 64>(fp, n_pre, s);
-  return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, n_pre, s) : launch_fwd_t<Fp16, 128>(fp, n_pre, s);
+  if (p.d <= 128)
+    return p.bf16 ? launch_fwd_t<Bf16, 128>(fp, n_pre, s) : launch_fwd_t<Fp16, 128>(fp, n_pre, s);
+  return p.bf16 ? launch_fwd_t<Bf16, 256>(fp, n_pre, s) : launch_fwd_t<Fp16, 256>(fp, n_pre, s);
 }
 
 }  // namespace thd
