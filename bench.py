@@ -11,7 +11,10 @@ heads, head_dim 128, bf16, dO ~ N(0,1).
 
 Before the W warm-up steps the same step runs untimed for --spinup-seconds:
 the first few hundred milliseconds under load run at lower clocks, which
-would otherwise make the timed steps depend on what ran before them.
+would otherwise make the timed steps depend on what ran before them.  The K
+timed steps are plain steps; a second pass of the same steps records HIP
+events between the kernels for the per-kernel times, and a third replays the
+step from one HIP graph (spun up the same way).
 
 Prints one JSON line.  `value` is valid-pair TFLOP/s of fwd+bwd (14*d FLOPs
 per valid (query, key) pair and head); `roofline` describes the dominant
@@ -247,23 +250,38 @@ def main():
         _lib.check(lib.thd_attn_bwd(args, P["q"], P["k"], P["v"], P["o"], P["do"], P["lse"],
                                     P["dq"], P["dk"], P["dv"], P["ws"], ws_bytes, st), "bwd")
 
-    t_spin = time.perf_counter()
-    while time.perf_counter() - t_spin < a.spinup_seconds:
-        for _ in range(10):
-            untimed_step()
-        torch.cuda.synchronize()
-    for i in range(a.warmup):
-        step(i)
+    def spin_up(run):
+        # the first few hundred milliseconds under load run at lower clocks
+        t_spin = time.perf_counter()
+        while time.perf_counter() - t_spin < a.spinup_seconds:
+            for _ in range(10):
+                run()
+            torch.cuda.synchronize()
+
+    # Timed region: K plain steps (nothing but the step's own launches).
+    spin_up(untimed_step)
+    for _ in range(a.warmup):
+        untimed_step()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(a.warmup, total):
-        step(i)
+    for _ in range(a.steps):
+        untimed_step()
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # The same steps again with HIP events recorded between the kernels, on
+    # the stream they run on, for the per-kernel times (the event records
+    # themselves leave gaps between kernels, so this pass is not the one the
+    # throughput is taken from).
+    for i in range(total):
+        step(i)
+    torch.cuda.synchronize()
+
     # The same step captured once in a HIP graph and replayed: the launches of
     # the eager step above cost host time between kernels, a replay does not.
-    # (Reported beside the eager figures; a capture failure only drops it.)
+    # The replays are spun up like the eager steps: after the idle time of the
+    # capture, the first replays run at lower clocks.  (Reported beside the
+    # eager figures; a capture failure only drops it.)
     def graph_time():
         g = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream(dev)  # default priority
@@ -275,6 +293,7 @@ def main():
         with torch.cuda.graph(g):
             untimed_step(_stream(dev))   # the capture stream
         torch.cuda.synchronize()
+        spin_up(g.replay)
         for _ in range(a.warmup):
             g.replay()
         torch.cuda.synchronize()
