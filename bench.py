@@ -60,7 +60,8 @@ def parse():
 # Sources each timed kernel is built from: a counter record of a kernel stays
 # valid while these files are unchanged.
 KERNEL_SOURCES = {
-    "thd_bwd_main_kernel": ("thd_bwd.hip", "thd_common.hpp", "thd_launch.hpp"),
+    "thd_bwd_dkdv_kernel": ("thd_bwd_dkdv.hip", "thd_bwd_split.hpp", "thd_common.hpp"),
+    "thd_bwd_dq_kernel": ("thd_bwd_split.hip", "thd_bwd_split.hpp", "thd_common.hpp"),
     "thd_fwd_kernel": ("thd_fwd.hip", "thd_common.hpp", "thd_launch.hpp"),
 }
 
@@ -318,9 +319,10 @@ def main():
         print(json.dumps(res), flush=True)
         return
     fwd_ms = [e[0].elapsed_time(e[1]) for e in timed]
+    # the backward's launches (head dims up to 128): pre pass, dq pass, dk/dv pass
     pre_ms = [e[2].elapsed_time(e[3]) for e in timed]
-    main_ms = [e[3].elapsed_time(e[4]) for e in timed]
-    post_ms = [e[4].elapsed_time(e[5]) for e in timed]
+    dq_ms = [e[3].elapsed_time(e[4]) for e in timed]
+    dkdv_ms = [e[4].elapsed_time(e[5]) for e in timed]
     mask_ms = [e[6].elapsed_time(e[0]) for e in timed]
     step_ms = sorted(e[6].elapsed_time(e[5]) for e in timed)
     mean = lambda xs: sum(xs) / len(xs)
@@ -331,7 +333,8 @@ def main():
     value = flops / (elapsed / a.steps) / 1e12
 
     kern = {"thd_fwd_kernel": (mean(fwd_ms), attention_flops(pairs, w.d, "fwd")),
-            "thd_bwd_main_kernel": (mean(main_ms), attention_flops(pairs, w.d, "bwd"))}
+            "thd_bwd_dq_kernel": (mean(dq_ms), attention_flops(pairs, w.d, "bwd_dq_pass")),
+            "thd_bwd_dkdv_kernel": (mean(dkdv_ms), attention_flops(pairs, w.d, "bwd_dkdv_pass"))}
     dom = max(kern, key=lambda n: kern[n][0])
     dom_ms, dom_flops = kern[dom]
     achieved = dom_flops / (dom_ms * 1e-3) / 1e12
@@ -339,7 +342,8 @@ def main():
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": (measured_traffic(dom, "16seq_causal_h16_d128") if w.name == "2" else None),
-                "avg_launch_ms": round(dom_ms, 4)}
+                "avg_launch_ms": round(dom_ms, 4),
+                "flops_per_launch": int(dom_flops)}
     busy = measured_busy("16seq_causal_h16_d128") if w.name == "2" else None
     if busy is not None:
         for kernel, rec in busy.items():
@@ -383,7 +387,7 @@ def main():
         },
         "kernel_ms": {"masks": round(mean(mask_ms), 4),
                       "fwd": round(mean(fwd_ms), 4), "bwd_pre": round(mean(pre_ms), 4),
-                      "bwd_main": round(mean(main_ms), 4), "bwd_post": round(mean(post_ms), 4)},
+                      "bwd_dq": round(mean(dq_ms), 4), "bwd_dkdv": round(mean(dkdv_ms), 4)},
         "roofline": roofline,
         "cpu_baseline": None,
     }

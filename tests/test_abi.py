@@ -139,9 +139,12 @@ def test_workspace_size_and_check():
     lib = _lib.load()
     a = _args()
     need = lib.thd_attn_bwd_workspace_size(ctypes.byref(a))
-    # fp32 dq accumulator [T_q, h_q, d], two fp32 row statistics [h_q, T_q]
-    # and the schedule of the key tiles
-    assert need >= 16 * 4 * 64 * 4 + 2 * 16 * 4 * 4 + (2 + 2 * (1 + 2)) * 4
+    # two fp32 row statistics [h_q, T_q], the dq pass's schedule of query
+    # tiles and the dk/dv pass's of key tiles (no fp32 dq accumulator at
+    # head dims up to 128); above 128, also the fp32 dq accumulator
+    assert need >= 2 * 16 * 4 * 4 + 2 * (2 + 2 * (1 + 2)) * 4
+    wide = lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(head_dim=192)))
+    assert wide >= 16 * 4 * 256 * 4 + 2 * 16 * 4 * 4
     assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(batch=-1))) == 0
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, need - 1, None) == -4
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, None, need, None) == -4

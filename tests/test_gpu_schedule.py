@@ -3,16 +3,17 @@ device, read back from their workspaces and compared with the order they are
 defined to have.
 
 Each schedule lists the (sequence, tile) items of its pass: query tiles of
-128 rows for the forward, key tiles of 256 keys for the backward.  An item's
-work W is the number of key tiles (forward, BN keys each: 32 at d > 32, 64
-at d <= 32) or 32-row query tiles (backward) it walks: all of them without a
-causal mask, else those up to the diagonal (top-left, or shifted by lk - lq
-for bottom-right).  The order: sequences by their largest item's work,
-largest first, ties in sequence order; within a sequence, its items largest
-first.  Workspace layouts (sizes from the library's own size queries):
-forward = the schedule; backward = fp32 dQ accumulator [T_q][h_q][DP], then
--D and -LSE/scale [2][h_q][T_q], then the schedule, each part starting on a
-256-byte boundary.  Schedule = int32 [count, unused, (b, t) per rank].
+128 rows for the forward and the backward's dq pass, key tiles of 256 keys
+for its dk/dv pass.  An item's work W is the number of key tiles (forward and
+dq pass, BN keys each: 32 at d > 32, 64 at d <= 32) or 32-row query tiles
+(dk/dv pass) it walks: all of them without a causal mask, else those up to
+the diagonal (top-left, or shifted by lk - lq for bottom-right).  The order:
+sequences by their largest item's work, largest first, ties in sequence
+order; within a sequence, its items largest first.  Workspace layouts (sizes
+from the library's own size queries): forward = the schedule; backward =
+-D and -LSE/scale [2][h_q][T_q], then the dq pass's schedule, then the dk/dv
+pass's, each part starting on a 256-byte boundary.  Schedule = int32 [count,
+unused, (b, t) per rank].
 Bit-exact comparison: the schedule is integer work.
 """
 import numpy as np
@@ -112,7 +113,9 @@ def test_schedules_match_definition(kw):
                  cu_seqlens_kv_padded=meta["cu_seqlens_kv_padded"],
                  is_causal=meta["is_causal"], batch_size=w.batch, workspace=ws_b)
     torch.cuda.synchronize()
-    dp = 32 if w.d <= 32 else 64 if w.d <= 64 else 128
-    off = align256(w.T_q * w.h_q * dp * 4) + align256(w.T_q * w.h_q * 2 * 4)
+    off_q = align256(w.T_q * w.h_q * 2 * 4)
+    n_qtiles = ceil_div(w.T_q, 128) + w.batch
+    off_k = off_q + align256((2 + 2 * n_qtiles) * 4)
+    assert read_schedule(ws_b, off_q) == exp_f
     exp_b = expected_schedule(w.lens_kv, w.lens_q, types, 256, 32, -8)
-    assert read_schedule(ws_b, off) == exp_b
+    assert read_schedule(ws_b, off_k) == exp_b

@@ -2,7 +2,8 @@
 
     python -m variable_length_packed_amd.build [--verbose]
 
-Compiles every ``csrc/*.hip`` into one shared library next to this file.
+Compiles every ``csrc/*.hip`` (one object each, under ``_build/``) and links
+them into one shared library next to this file.
 """
 import glob
 import os
@@ -26,8 +27,9 @@ def hipcc_path():
     raise RuntimeError("hipcc not found; ROCm is required to build libthdattn.so")
 
 
-def compile_flags():
-    return [
+def compile_flags(source=None):
+    """hipcc flags for one source (all of them when source is None)."""
+    flags = [
         f"--offload-arch={ARCH}",
         "-O3",
         "-std=c++17",
@@ -36,32 +38,53 @@ def compile_flags():
         "-Wno-unused-function",
         # keep hipcc from forming packed fp32 ops on its own
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA results in VGPRs: the softmax / gradient VALU work reads them
-        # directly instead of copying them out of AGPRs
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
         f"-I{INCLUDE}",
         f"-I{CSRC}",
     ]
+    # MFMA results in VGPRs: the softmax / gradient VALU work reads them
+    # directly instead of copying them out of AGPRs
+    flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    return flags
 
 
 def build_library(verbose=False, extra_flags=()):
-    """Compile csrc/*.hip into LIB_PATH.  Always recompiles."""
+    """Compile csrc/*.hip into LIB_PATH (one object per source, in parallel,
+    then one link).  Always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
     sources = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not sources:
         raise RuntimeError(f"no HIP sources under {CSRC}")
+    hipcc = hipcc_path()
+    objdir = os.path.join(PKG_DIR, "_build")
+    os.makedirs(objdir, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(objdir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *compile_flags(src), *extra_flags, "-c", "-o", obj, src]
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        return src, obj, res
+
+    jobs = min(len(sources), max(1, min(8, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(compile_one, sources))
+    for src, obj, res in results:
+        if res.returncode != 0:
+            sys.stderr.write(res.stdout + res.stderr)
+            raise RuntimeError(f"hipcc failed on {os.path.basename(src)} (exit {res.returncode})")
+        if verbose and res.stderr:
+            # hipcc's host pass warns about the device-only target feature
+            lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
+            if lines:
+                sys.stderr.write("\n".join(lines) + "\n")
     tmp = LIB_PATH + ".tmp"
-    cmd = [hipcc_path(), *compile_flags(), *extra_flags, "-shared", "-o", tmp, *sources]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+    cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+           *[obj for _, obj, _ in results]]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError(f"hipcc failed with exit code {res.returncode}")
-    if verbose and res.stderr:
-        # hipcc's host pass warns about the device-only target feature
-        lines = [ln for ln in res.stderr.splitlines() if "packed-fp32-ops" not in ln]
-        if lines:
-            sys.stderr.write("\n".join(lines) + "\n")
+        raise RuntimeError(f"hipcc link failed with exit code {res.returncode}")
     os.replace(tmp, LIB_PATH)
     return LIB_PATH
 

@@ -1,4 +1,6 @@
-// Backward attention over packed variable-length ("thd") tensors.
+// Backward attention over packed variable-length ("thd") tensors, head dims
+// above 128 (136 .. 256; smaller head dims take the two-pass backward of
+// thd_bwd_split.hip).
 //
 // Gradients of sum(O * dO) w.r.t. Q, K and V for the forward in thd_fwd.hip
 // (TransformerEngine PR "Add per-sequence causal policy to packed THD
@@ -9,18 +11,13 @@
 //   dS = P * (dP - D) with D = rowsum(dO * O),
 //   dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches:
-//   pre  : -D per (row, head), zeroing of the fp32 dQ accumulator, and the
-//          main kernel's schedule (key tiles grouped by sequence, each
-//          sequence's largest first);
-//   main : one workgroup of 8 waves per (sequence, 256-key tile, kv head),
-//          in schedule order; wave w owns 32 keys and keeps dK^T and dV^T in
-//          registers (K and V sit in LDS) while the workgroup walks the
-//          32-row query tiles (from the diagonal when causal) of every query
-//          head of its GQA group.  dQ of a query tile is computed by the
-//          whole workgroup from dS staged in LDS (wave w takes d columns
-//          16w..16w+15 over all 256 keys) and added to the accumulator with
-//          fp32 atomics;
+// Three launches, correct first and not tuned:
+//   pre  : -D per (row, head), -LSE/scale, zeroing of the fp32 dQ
+//          accumulator, and the main kernel's schedule (key tiles grouped by
+//          sequence, each sequence's largest first);
+//   main : one workgroup of 4 waves per (sequence, 64-key tile, kv head); dK
+//          and dV of a tile in registers, dQ of each query tile added to the
+//          accumulator with fp32 atomics;
 //   post : dQ accumulator -> storage dtype, zeros on pad rows of dK and dV.
 #include <type_traits>
 
@@ -31,9 +28,8 @@ namespace thd {
 
 namespace {
 
-constexpr int kBwdBK = 256;  // keys per workgroup (head dims up to 128)
 constexpr int kBwdBQ = 32;   // query rows per step
-constexpr int kWideBK = 64;  // keys per workgroup of the head dims above 128
+constexpr int kWideBK = 64;  // keys per workgroup
 constexpr int kZeroRowsB = 64;
 
 struct BwdParams {
@@ -96,9 +92,9 @@ struct BwdSchedModel {
   }
 };
 
-// Keys per workgroup of the main kernel for a padded head dim.
+// Keys per workgroup of the main kernel.
 template <int DP>
-constexpr int kMainBK = DP > 128 ? kWideBK : kBwdBK;
+constexpr int kMainBK = kWideBK;
 
 // (row, head) pairs per pre / post workgroup: KCH = DP / 8 lanes per pair
 // (one 16-byte chunk each), 256 / KCH lane groups, two pairs per group.
@@ -168,449 +164,6 @@ __global__ __launch_bounds__(256) void thd_bwd_pre_kernel(BwdParams p) {
       else p.lsum[si[t]] = lse_v[t] * (-1.0f / p.scale);   // -LSE / scale
     }
   }
-}
-
-// ---------------------------------------------------------------------------
-// main
-// ---------------------------------------------------------------------------
-// One workgroup of 8 waves per (sequence, 256-key tile, kv head); wave w owns
-// keys 32w .. 32w+31 and keeps dK^T / dV^T for them in registers.  All waves
-// walk the same 32-row query tiles (every query head of the GQA group, from
-// the diagonal when causal).  dQ of a query tile is formed by the whole
-// workgroup from dS staged in LDS -- wave w takes d columns 16w .. 16w+15 over
-// all 256 keys with 16x16x32 products -- and added to the fp32 accumulator:
-// one atomic add per (query row, d column) per 256 keys.
-//
-// LDS (bytes, DP = 128): dS 16K, Q 8K, dO 8K, K 64K and V 64K (resident) =
-// 160K, in that order so that every tile but V starts below 64K and can be
-// addressed through the instruction's offset field.  Q, dO, K and V are
-// row-major with swizzled 16-byte chunks; Q^T, dO^T and K^T operands come
-// from transpose reads.
-template <int DP>
-__device__ __forceinline__ uint32_t swz_ds(int row, int kv) {
-  // dS tile [32][256]: chunk index XOR row%16 keeps 16 rows read at one
-  // logical chunk in 16 distinct bank groups
-  return (uint32_t)row * 512u + ((uint32_t)((kv >> 3) ^ (row & 15)) << 4) + (uint32_t)(kv & 7) * 2;
-}
-
-// Swizzled addresses inside the loop.  With the swizzle f(row) an XOR on the
-// chunk index that depends on row bits 0-3 only, each address the loop uses
-// equals a per-lane base XOR a constant: the constant either flips chunk
-// bits or sets row bits that are zero in the base.  The loop therefore keeps
-// a handful of bases live instead of one register per address.
-//   S / dP operands:   swz(r, 16c + 8h)         = swz(r, 8h) ^ (c << 5)
-//                      (same for key row 32w + r, since f(32w + r) = f(r))
-//   dV / dK operands:  swz(R + 16kb + 8j, C + 32dt) = swz(R, C) ^ tr_xor(dt, kb, j)
-//   dS writes:         swz_ds(8m + 4h + e, kv)  = swz_ds(4h, kv) ^ ((8m + e) << 9)
-//                                                 ^ ((8(m & 1) + e) << 4)
-//   dQ, dS reads:      swz_ds(16qh + g, 32st + 8grp) = swz_ds(g, 8grp) ^ (qh << 13)
-//                                                      ^ (st << 6)
-//   dQ, K^T reads:     swz(32st + R' + 4j, C), R' = 8grp + tr_row
-//                        = swz(R', C) ^ ((32st + 4j) * 2DP) ^ (j << 4)
-__device__ __forceinline__ uint32_t ds_xor(int m, int e) {
-  return ((uint32_t)(8 * m + e) << 9) ^ ((uint32_t)(8 * (m & 1) + e) << 4);
-}
-
-template <class DT, int DP>
-__global__ __launch_bounds__(512, 1) void thd_bwd_main_kernel(BwdParams p) {
-  constexpr int BK = kBwdBK, BQ = kBwdBQ;
-  constexpr int NC = DP / 16;
-  constexpr int ND = DP / 32;
-  constexpr int KCH = DP / 8;
-  constexpr int TILE = BQ * DP * 2;
-  constexpr int OFF_DS = 0;
-  constexpr int OFF_Q = OFF_DS + BQ * BK * 2;
-  constexpr int OFF_DO = OFF_Q + TILE;
-  constexpr int OFF_K = OFF_DO + TILE;
-  constexpr int OFF_V = OFF_K + BK * DP * 2;
-  constexpr int SMEM = OFF_V + BK * DP * 2;
-  static_assert(SMEM <= 163840, "LDS budget of one workgroup");
-  static_assert(OFF_K < 65536, "tiles read through the offset field start below 64K");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  unsigned char* Kt = smem + OFF_K;
-  unsigned char* Vt = smem + OFF_V;
-  unsigned char* Qb = smem + OFF_Q;
-  unsigned char* Ob = smem + OFF_DO;
-  unsigned char* dSs = smem + OFF_DS;
-
-  // Workgroups in schedule order (by sequence, largest items first), kv heads
-  // minor: the key tiles of a (sequence, head) run together on one XCD and
-  // share its Q, dO and row statistics in L2.
-  const int bid = blockIdx.x;
-  const int rk = bid / p.h_kv;
-  const int hk = bid - rk * p.h_kv;
-  if (rk >= p.sched[0]) return;
-  const int b = uniform(p.sched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
-  if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
-
-  const int tid = threadIdx.x;
-  const int w = uniform(tid >> 6);  // keys 32w .. 32w+31; dQ columns 16w .. 16w+15
-  const int l = tid & 63;
-  const int r = l & 31;
-  const int h = l >> 5;
-  const int g16 = l & 15;           // lane inside its 16-lane group
-  const int grp = l >> 4;           // 16-lane group of the wave
-
-  const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
-  const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const uint32_t accrow_bytes = (uint32_t)p.h_q * DP * 4;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
-  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const int mtype = mask_type_of(p.causal, b);
-  const bool causal = mask_is_causal(mtype);
-  const int off = causal_offset(mtype, lq, lk);  // key j visible to query i iff j <= i + off
-  const int k0 = tile_in_seq * BK;
-  if (k0 >= lk) return;
-  const int kw0 = k0 + 32 * w;
-  const int my_k = kw0 + r;
-
-  // Keys [k0, lk) of kv head hk -> LDS; rows past lk read as zeros.
-  const uint16_t* kbase = p.k + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
-  const uint16_t* vbase = p.v + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d;
-  const uint32_t kv_bytes = (uint32_t)(lk - k0) * kvrow_bytes;
-  // Straight from memory into LDS: load i of wave w fills 1 KB block
-  // 8i + w of each tile, lane l the 16-byte slot 64(8i + w) + l, i.e. row
-  // slot / KCH at swizzled chunk position slot % KCH, which holds the row's
-  // memory chunk (slot % KCH) ^ f(row).  Waited for before the barrier below.
-  {
-    static_assert(BK * KCH % 512 == 0, "whole 1 KB blocks per wave");
-    const u32x4 k_rs = rsrc_words(kbase, kv_bytes);
-    const u32x4 v_rs = rsrc_words(vbase, kv_bytes);
-    const uint32_t k_lds = lds_addr(Kt), v_lds = lds_addr(Vt);
-#pragma unroll
-    for (int i = 0; i < BK * KCH / 512; ++i) {
-      const int slot = 64 * (8 * i + w) + l;
-      const int row = slot / KCH;
-      const int x = slot - row * KCH;
-      const int gc = x ^ (int)((swz<DP>(row, 0) >> 4) & (KCH - 1));
-      const uint32_t off = 8 * gc < p.d ? (uint32_t)row * kvrow_bytes + 16u * gc : kOobOffset;
-      buf_load_lds16(k_rs, k_lds + 1024u * (8 * i + w), off);
-      buf_load_lds16(v_rs, v_lds + 1024u * (8 * i + w), off);
-    }
-  }
-
-  // Query tiles: from the first tile that can see key k0 when causal
-  // (query k0 - off).
-  const int q_start = causal ? max(floor_div(k0 - off, BQ), 0) * BQ : 0;
-  const int n_qt = (lq > q_start) ? (lq - q_start + BQ - 1) / BQ : 0;
-  const int n_iter = p.group * n_qt;
-
-  // Staging of the next query tile: BQ*KCH chunks each of Q and dO.
-  const bool s_loader = tid < BQ * KCH;
-  const int s_row = tid / KCH;
-  const int s_x = tid - s_row * KCH;
-  const uint32_t s_off = (s_loader && 8 * s_x < p.d) ? (uint32_t)s_row * qrow_bytes + 16u * s_x
-                                                      : kOobOffset;
-  u32x4 qreg = {0u, 0u, 0u, 0u}, oreg = {0u, 0u, 0u, 0u};
-  // Always issued (past the last tile with an out-of-range offset), so that
-  // every path through the loop has the same vector memory operations in
-  // flight and waits can be counted exactly.
-  auto load_q = [&](int hq, int q0, bool real) {
-    const int64_t hoff = sq * (int64_t)p.h_q * p.d + (int64_t)hq * p.d;
-    const rsrc_t q_rs = make_rsrc(p.q + hoff, (uint32_t)lq * qrow_bytes);
-    const rsrc_t o_rs = make_rsrc(p.dout + hoff, (uint32_t)lq * qrow_bytes);
-    const uint32_t off =
-        (s_off == kOobOffset || !real) ? kOobOffset : s_off + (uint32_t)q0 * qrow_bytes;
-    qreg = buf_load16(q_rs, off, 0);
-    oreg = buf_load16(o_rs, off, 0);
-  };
-  auto store_q = [&]() {
-    if (s_loader) {
-      *(u32x4*)(Qb + swz<DP>(s_row, 8 * s_x)) = qreg;
-      *(u32x4*)(Ob + swz<DP>(s_row, 8 * s_x)) = oreg;
-    }
-  };
-
-  f32x16 dk_acc[ND], dv_acc[ND];
-#pragma unroll
-  for (int i = 0; i < ND; ++i) {
-    dk_acc[i] = f32x16{};
-    dv_acc[i] = f32x16{};
-  }
-
-  // Transpose-read addressing: lane s of a 16-lane group reads row
-  // R0 + s/4, columns C0 + 4*(s%4) .. +3.
-  const int tr_row = g16 >> 2;
-  const int tr_col = 4 * (g16 & 3);
-  const float c2 = p.c2;
-  // address bases (relative to their tile)
-  const uint32_t b_q = swz<DP>(r, 8 * h);
-  const uint32_t b_k = swz<DP>(32 * w + r, 8 * h);
-  const uint32_t b_t = swz<DP>(4 * h + tr_row, 16 * (grp & 1) + tr_col);
-  const uint32_t b_s = swz_ds<DP>(4 * h, 32 * w + r);
-  const uint32_t b_d = swz_ds<DP>(g16, 8 * grp);
-  const uint32_t b_kt = swz<DP>(8 * grp + tr_row, 16 * w + tr_col);
-
-  int hq = hk * p.group, q0 = q_start;
-  auto advance = [&](int& hq_, int& q0_) {
-    q0_ += BQ;
-    if (q0_ >= lq) {
-      q0_ = q_start;
-      ++hq_;
-    }
-  };
-  // dQ of a query tile is held in registers until the next iteration has
-  // issued its loads: vector memory operations retire in order, so atomics
-  // issued before those loads would make every wait for them wait for the
-  // atomics as well.  Atomics are always issued; those with nothing to add
-  // (first iteration, d columns past DP) go out of range and are dropped.
-  f32x4_t dq[2] = {f32x4_t{}, f32x4_t{}};
-  int hq_p = hq, q0_p = q0;  // query tile that dq belongs to
-  const int dcol = 16 * w + g16;
-  // Atomic j (0..7) adds dq[j / 4][j % 4] to row q0 + 4grp + 16(j / 4) + j % 4
-  // of the accumulator ([T_q][h_q][DP]; the resource starts at this head's
-  // first row of the sequence, rows accrow_bytes apart): rows past lq fall
-  // outside the resource and are dropped.
-  rsrc_t acc_rs;
-  uint32_t acc_base = kOobOffset;
-  auto setup_dq = [&](bool real) {
-    acc_rs = make_rsrc(p.dq_acc + (sq * p.h_q + hq_p) * DP, (uint32_t)lq * accrow_bytes);
-    acc_base = (real && dcol < p.d) ? (uint32_t)(q0_p + 4 * grp) * accrow_bytes + dcol * 4u
-                                    : kOobOffset;
-  };
-  auto atomic_dq = [&](int j) {
-    const int qh = j >> 2, e = j & 3;
-    buf_atomic_add(dq[qh][e], acc_rs,
-                   acc_base == kOobOffset ? kOobOffset
-                                          : acc_base + (uint32_t)(16 * qh + e) * accrow_bytes,
-                   0);
-  };
-  auto flush_dq = [&](bool real) {
-    setup_dq(real);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) atomic_dq(j);
-  };
-
-  // The products start from the row statistics of this lane's query rows
-  // q0 + 8m + 4h + e (register 4m + e of the C layout): S from -LSE/scale,
-  // so that P = exp2(S * scale * log2 e), and dP from -D, so that
-  // dS = P * dP.  They are loaded one query tile ahead, into the S and dP
-  // registers themselves once the previous tile is done with them; the last
-  // load goes out of range.
-  f32x16 s, dp;
-  // Load j (0..7): rows 8m + 4h .. +3 (m = j / 2) of -LSE/scale (j even) or
-  // -D (j odd) into S or dP registers 4m .. 4m+3.
-  rsrc_t l_rs, d_rs;
-  uint32_t st_off = kOobOffset;
-  auto setup_stats = [&](int hq_, int q0_, bool real) {
-    const int64_t roff = real ? (int64_t)hq_ * p.T_q + sq : 0;
-    l_rs = make_rsrc(p.lsum + roff, (uint32_t)lq * 4u);
-    d_rs = make_rsrc(p.dsum + roff, (uint32_t)lq * 4u);
-    st_off = real ? (uint32_t)(q0_ + 4 * h) * 4u : kOobOffset;
-  };
-  auto load_stat = [&](int j) {
-    const int m = j >> 1;
-    const uint32_t off = st_off == kOobOffset ? kOobOffset : st_off + 32u * m;
-    const f32x4 v = __builtin_bit_cast(f32x4, buf_load16((j & 1) ? d_rs : l_rs, off, 0));
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (j & 1)
-        dp[4 * m + e] = v[e];
-      else
-        s[4 * m + e] = v[e];
-    }
-  };
-  auto load_stats = [&](int hq_, int q0_, bool real) {
-    setup_stats(hq_, q0_, real);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) load_stat(j);
-  };
-
-  if (n_iter > 0) {
-    load_stats(hq, q0, true);
-    load_q(hq, q0, true);
-    store_q();
-  }
-  // vmcnt(0): this wave's K and V blocks are in LDS (the compiler does not
-  // count those loads), and so are the first tile's statistics.
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  __syncthreads();  // K, V and the first query tile visible
-  for (int iter = 0; iter < n_iter; ++iter) {
-    const bool more = iter + 1 < n_iter;
-    int hq_n = hq, q0_n = q0;
-    advance(hq_n, q0_n);
-
-    load_q(hq_n, q0_n, more);
-    // The previous tile's dQ atomics and the next tile's row statistics are
-    // spread over the product loops below (one or more per step), where they
-    // issue while the matrix cores work.
-    setup_dq(iter > 0);
-    setup_stats(hq_n, q0_n, more);
-    constexpr int kVm = 8 / NC;  // atomics or loads per step (NC = 2 * ND)
-
-    // Every wave runs the same path (a wave none of whose keys is visible to
-    // this query tile is masked to zeros), so that all of them issue the same
-    // vector memory operations in the same order and the waits stay exact.
-    {
-      // Software pipelined: the operands of step c + 1 are read before the
-      // products of step c, and the scheduler is kept from undoing it.
-      // (V lies past the offset field's reach, so it gets its own base.)
-      const uint32_t a_q = opaque(b_q), a_k = opaque(b_k), a_v = opaque(b_k + OFF_V);
-      u32x4 qa[2], ka[2], oa[2], va[2];
-      auto ld_s = [&](int c, int slot) {
-        const uint32_t cx = (uint32_t)c << 5;
-        qa[slot] = *(const u32x4*)(Qb + (a_q ^ cx));
-        ka[slot] = *(const u32x4*)(Kt + (a_k ^ cx));
-        oa[slot] = *(const u32x4*)(Ob + (a_q ^ cx));
-        va[slot] = *(const u32x4*)(smem + (a_v ^ cx));
-      };
-      ld_s(0, 0);
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        if (c + 1 < NC) ld_s(c + 1, (c + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        s = DT::mfma(as_vec8<DT>(qa[c & 1]), as_vec8<DT>(ka[c & 1]), s);
-        dp = DT::mfma(as_vec8<DT>(oa[c & 1]), as_vec8<DT>(va[c & 1]), dp);
-#pragma unroll
-        for (int j = 0; j < kVm; ++j) atomic_dq(kVm * c + j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // mask: key past lk, query row past lq, or (causal) key after the row.
-      // Only tiles on the diagonal or at a sequence's end need it; a masked
-      // score becomes -inf, whose exp2 is 0.
-      const bool need_mask =
-          (kw0 + 32 > lk) || (q0 + BQ > lq) || (causal && kw0 + 31 > q0 + off);
-      if (__builtin_expect(need_mask, 0)) {
-        const int lim_lo = causal ? my_k - q0 - off : -1;  // visible iff qi >= my_k - off - q0
-        const int row_hi = my_k < lk ? lq - q0 : 0;  // visible iff qi < lq - q0
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
-          if (!(qi >= lim_lo && qi < row_hi)) s[i] = -__builtin_inff();
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = __builtin_amdgcn_exp2f(s[i] * c2);
-        s[i] = pv;
-        dp[i] = pv * dp[i];
-      }
-      typename DT::vec8 pb[2], db[2];
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        float tp[8], td[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          tp[j] = s[8 * kb + j];
-          td[j] = dp[8 * kb + j];
-        }
-        pb[kb] = pack8<DT>(tp);
-        db[kb] = pack8<DT>(td);
-      }
-      // dV^T += dO^T P and dK^T += Q^T dS.  A operand lane (r, h) needs
-      // column d = 32dt + r at query slots q = 16kb + {4h..4h+3, 8+4h..8+4h+3},
-      // the order in which P / dS hold them: two transpose reads.
-      const uint32_t a_t = opaque(b_t);
-      u32x4 to[2], tq[2];
-      auto ld_t = [&](int i, int slot) {
-        const int dt = i >> 1, kb = i & 1;
-        const uint32_t t0 = a_t ^ tr_xor<DP>(dt, kb, 0);
-        const uint32_t t1 = a_t ^ tr_xor<DP>(dt, kb, 1);
-        to[slot] = cat2(lds_read_tr(Ob, t0), lds_read_tr(Ob, t1));
-        tq[slot] = cat2(lds_read_tr(Qb, t0), lds_read_tr(Qb, t1));
-      };
-      ld_t(0, 0);
-#pragma unroll
-      for (int i = 0; i < 2 * ND; ++i) {
-        const int dt = i >> 1, kb = i & 1;
-        if (i + 1 < 2 * ND) ld_t(i + 1, (i + 1) & 1);
-        __builtin_amdgcn_sched_barrier(0);
-        dv_acc[dt] = DT::mfma(as_vec8<DT>(to[i & 1]), pb[kb], dv_acc[dt]);
-        dk_acc[dt] = DT::mfma(as_vec8<DT>(tq[i & 1]), db[kb], dk_acc[dt]);
-#pragma unroll
-        for (int j = 0; j < kVm; ++j) load_stat(kVm * i + j);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // dS (query-major) for the dQ product; elements are taken from the
-      // packed 32-bit words (element j sits in word j/2, half j&1).
-      const uint32_t a_s = opaque(b_s);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const u32x4 words = __builtin_bit_cast(u32x4, db[kb]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int i = 8 * kb + j;
-          *(uint16_t*)(dSs + (a_s ^ ds_xor(i >> 2, i & 3))) =
-              (uint16_t)(words[j >> 1] >> (16 * (j & 1)));
-        }
-      }
-    }
-    __syncthreads();  // dS complete; every wave is done with this query tile
-    if (more) store_q();
-
-    if (16 * w < DP) {
-      // dQ[q][16w + n] = sum_kv dS[q][kv] K[kv][16w + n] over the workgroup's
-      // keys.  16x16x32 products: A lane l = dS[qh*16 + l%16][32s + 8(l/16) ..],
-      // B lane l = K[32s + 8(l/16) + j][16w + l%16] (two transpose reads).
-      int kv_act = lk - k0;
-      if (kv_act > BK) kv_act = BK;
-      if (causal && q0 + BQ + off - k0 < kv_act) kv_act = q0 + BQ + off - k0;
-      const int nst = (kv_act + 31) / 32;
-      const uint32_t a_d = opaque(b_d), a_kt = opaque(b_kt);
-      dq[0] = f32x4_t{};
-      dq[1] = f32x4_t{};
-      // Software pipelined like the products above.  The read for the step
-      // after the last is clamped to a step inside the tiles (and unused), so
-      // that every iteration has the same reads in flight.
-      u32x4 kt[2], da0[2], da1[2];
-      auto ld_q = [&](int st, int slot) {
-        const uint32_t k_x = (uint32_t)(32 * st) * (DP * 2);
-        kt[slot] = cat2(lds_read_tr(Kt, a_kt ^ k_x),
-                        lds_read_tr(Kt, a_kt ^ (k_x ^ ((uint32_t)(4 * DP * 2) | 16u))));
-        da0[slot] = *(const u32x4*)(dSs + (a_d ^ ((uint32_t)st << 6)));
-        da1[slot] = *(const u32x4*)(dSs + (a_d ^ ((1u << 13) | ((uint32_t)st << 6))));
-      };
-      ld_q(0, 0);
-      for (int st = 0; st < nst; st += 2) {
-        ld_q(min(st + 1, BK / 32 - 1), 1);
-        __builtin_amdgcn_sched_barrier(0);
-        dq[0] = DT::mfma16(as_vec8<DT>(da0[0]), as_vec8<DT>(kt[0]), dq[0]);
-        dq[1] = DT::mfma16(as_vec8<DT>(da1[0]), as_vec8<DT>(kt[0]), dq[1]);
-        __builtin_amdgcn_sched_barrier(0);
-        if (st + 1 >= nst) break;
-        ld_q(min(st + 2, BK / 32 - 1), 0);
-        __builtin_amdgcn_sched_barrier(0);
-        dq[0] = DT::mfma16(as_vec8<DT>(da0[1]), as_vec8<DT>(kt[1]), dq[0]);
-        dq[1] = DT::mfma16(as_vec8<DT>(da1[1]), as_vec8<DT>(kt[1]), dq[1]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      hq_p = hq;
-      q0_p = q0;
-    }
-    __syncthreads();  // next query tile visible; dS reads done
-    hq = hq_n;
-    q0 = q0_n;
-  }
-  if (n_iter > 0) flush_dq(16 * w < DP);
-
-  // Epilogue: this lane's key row of dK (scaled) and dV; rows past lk dropped.
-  const rsrc_t dk_rs = make_rsrc(p.dk + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
-  const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
-                                 kv_bytes);
-  const uint32_t krow = (uint32_t)(32 * w + r) * kvrow_bytes;
-#pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-    for (int gq = 0; gq < 4; ++gq) {
-      const int dd = 32 * dt + 8 * gq + 4 * h;
-      if (dd < p.d) {
-        u32x2 ok, ov;
-        ok[0] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 0] * p.scale) |
-                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 1] * p.scale) << 16);
-        ok[1] = (uint32_t)DT::bits(dk_acc[dt][4 * gq + 2] * p.scale) |
-                ((uint32_t)DT::bits(dk_acc[dt][4 * gq + 3] * p.scale) << 16);
-        ov[0] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 0]) |
-                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 1]) << 16);
-        ov[1] = (uint32_t)DT::bits(dv_acc[dt][4 * gq + 2]) |
-                ((uint32_t)DT::bits(dv_acc[dt][4 * gq + 3]) << 16);
-        buf_store8(ok, dk_rs, krow + 2u * dd, 0);
-        buf_store8(ov, dv_rs, krow + 2u * dd, 0);
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -981,10 +534,8 @@ hipError_t launch_bwd_t(const BwdParams& bp, hipStream_t s, hipEvent_t const* ev
   }
   if ((em = mark(1)) != hipSuccess) return em;
   if (bp.n_main > 0) {
-    if constexpr (DP > 128)
-      hipLaunchKernelGGL((thd_bwd_main_wide_kernel<DT>), dim3(bp.n_main), dim3(256), 0, s, bp);
-    else
-      hipLaunchKernelGGL((thd_bwd_main_kernel<DT, DP>), dim3(bp.n_main), dim3(512), 0, s, bp);
+    static_assert(DP == 256, "head dims up to 128 take the two-pass backward");
+    hipLaunchKernelGGL((thd_bwd_main_wide_kernel<DT>), dim3(bp.n_main), dim3(256), 0, s, bp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1006,15 +557,15 @@ int padded_dim(int d) { return d <= 32 ? 32 : d <= 64 ? 64 : d <= 128 ? 128 : 25
 
 }  // namespace
 
-static int64_t kv_tile_bound(const Problem& p) {
-  const int bk = p.d > 128 ? kWideBK : kBwdBK;
-  return (p.T_kv + bk - 1) / bk + p.batch;
-}
+static int64_t kv_tile_bound(const Problem& p) { return (p.T_kv + kWideBK - 1) / kWideBK + p.batch; }
 
-// fp32 dq accumulator [h_q][T_q][DP] (DP = head_dim rounded up to 32, 64,
-// 128 or 256), then -D = -rowsum(dO * O) and -LSE / scale (each [h_q][T_q]), then
+// Head dims up to 128: the two-pass backward's workspace.  Above: the fp32 dq
+// accumulator [T_q][h_q][256], then -D = -rowsum(dO * O) and -LSE / scale (each [h_q][T_q]), then
 // the main kernel's schedule (2 + 2 * key-tile bound int32).
+static bool use_split(const Problem& p) { return p.d <= 128; }
+
 size_t bwd_workspace_bytes(const Problem& p) {
+  if (use_split(p)) return split_bwd_workspace_bytes(p);
   const size_t acc = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
   const size_t dsum = align256((size_t)p.T_q * p.h_q * 2 * sizeof(float));
   const size_t sched = align256((size_t)(2 + 2 * kv_tile_bound(p)) * sizeof(int32_t));
@@ -1024,6 +575,8 @@ size_t bwd_workspace_bytes(const Problem& p) {
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
                       void* dv, void* workspace, hipStream_t s, hipEvent_t const* ev) {
+  if (use_split(p))
+    return launch_bwd_split(p, q, k, v, o, dout, lse, dq, dk, dv, workspace, s, ev);
   BwdParams bp;
   bp.q = (const uint16_t*)q;
   bp.k = (const uint16_t*)k;
@@ -1058,10 +611,6 @@ hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void
   bp.n_kv_tiles = (int)n_kv_tiles;
   bp.n_main = (p.batch > 0) ? (int)(n_kv_tiles * p.h_kv) : 0;
   bp.n_sched = (p.batch > 0) ? (p.batch + 3) / 4 : 0;
-  if (p.d <= 32) return p.bf16 ? launch_bwd_t<Bf16, 32>(bp, s, ev) : launch_bwd_t<Fp16, 32>(bp, s, ev);
-  if (p.d <= 64) return p.bf16 ? launch_bwd_t<Bf16, 64>(bp, s, ev) : launch_bwd_t<Fp16, 64>(bp, s, ev);
-  if (p.d <= 128)
-    return p.bf16 ? launch_bwd_t<Bf16, 128>(bp, s, ev) : launch_bwd_t<Fp16, 128>(bp, s, ev);
   return p.bf16 ? launch_bwd_t<Bf16, 256>(bp, s, ev) : launch_bwd_t<Fp16, 256>(bp, s, ev);
 }
 

@@ -5,7 +5,10 @@ sequence with lq queries and lk keys, lq*lk under the ``padding`` mask type,
 sum_i min(i+1, lk) under top-left ``padding_causal`` and
 sum_i clamp(i+1+lk-lq, 0, lk) under ``padding_causal_bottom_right``.  FLOPs count two per
 multiply-add of each matrix product: forward 2 products (QK^T, PV) = 4*d per
-pair; backward 5 products (S recompute, dP, dV, dK, dQ) = 10*d per pair.
+pair; backward 5 products (S recompute, dP, dV, dK, dQ) = 10*d per pair, the
+convention the throughput metric is quoted in.  The two passes of the backward
+for head dims up to 128 form S and dP once each: the dq pass does 3 products
+(S, dP, dQ: 6*d per pair), the dk/dv pass 4 (S, dP, dV, dK: 8*d per pair).
 """
 import numpy as np
 
@@ -32,5 +35,5 @@ def valid_pairs(lens_q, lens_kv, causal, h_q=1):
 
 
 def attention_flops(pairs, d, part="fwd+bwd"):
-    per = {"fwd": 4, "bwd": 10, "fwd+bwd": 14}[part]
+    per = {"fwd": 4, "bwd": 10, "fwd+bwd": 14, "bwd_dq_pass": 6, "bwd_dkdv_pass": 8}[part]
     return per * int(d) * int(pairs)
