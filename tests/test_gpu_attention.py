@@ -104,6 +104,12 @@ SMALL = [
          slot_multiple=128, gap_before=1),
     dict(seed=125, batch=4, max_len=220, h_q=2, d=160, dtype="fp16", causal="types",
          cross=True),
+    # long walks per key tile (max_seqlen_q x GQA group above 4096): the dk/dv
+    # pass's 256-key shape; every other small layout takes the 128-key one
+    dict(seed=126, batch=4, max_len=600, h_q=8, h_kv=1, d=128, dtype="bf16", causal="types",
+         cross=True),
+    dict(seed=127, batch=3, max_len=1500, h_q=8, h_kv=1, d=64, dtype="fp16", causal="mixed",
+         slot_multiple=64, gap_before=1),
 ]
 
 

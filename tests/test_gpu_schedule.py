@@ -3,8 +3,8 @@ device, read back from their workspaces and compared with the order they are
 defined to have.
 
 Each schedule lists the (sequence, tile) items of its pass: query tiles of
-128 rows for the forward and the backward's dq pass, key tiles of 256 keys
-for its dk/dv pass.  An item's work W is the number of key tiles (forward and
+128 rows for the forward and the backward's dq pass, key tiles of 128 or 256
+keys for its dk/dv pass.  An item's work W is the number of key tiles (forward and
 dq pass, BN keys each: 32 at d > 32, 64 at d <= 32) or 32-row query tiles
 (dk/dv pass) it walks: all of them without a causal mask, else those up to
 the diagonal (top-left, or shifted by lk - lq for bottom-right).  The order:
@@ -114,8 +114,11 @@ def test_schedules_match_definition(kw):
                  is_causal=meta["is_causal"], batch_size=w.batch, workspace=ws_b)
     torch.cuda.synchronize()
     off_q = align256(w.T_q * w.h_q * 2 * 4)
-    n_qtiles = ceil_div(w.T_q, 128) + w.batch
+    n_qtiles = ceil_div(w.T_q, 128) + w.batch   # the dq pass's query-tile bound
     off_k = off_q + align256((2 + 2 * n_qtiles) * 4)
     assert read_schedule(ws_b, off_q) == exp_f
-    exp_b = expected_schedule(w.lens_kv, w.lens_q, types, 256, 32, -8)
+    # key tiles of the dk/dv pass: 128 keys when max_seqlen_q times the GQA
+    # group is at most 4096, else 256
+    bk = 128 if w.max_seqlen_q * (w.h_q // w.h_kv) <= 4096 else 256
+    exp_b = expected_schedule(w.lens_kv, w.lens_q, types, bk, 32, -(bk // 32))
     assert read_schedule(ws_b, off_k) == exp_b

@@ -1,8 +1,8 @@
 // dk/dv pass of the backward for head dims up to 128 (see thd_bwd_split.hip
 // for the whole backward and its sources).
 //
-// One workgroup per (sequence, 256-key tile, kv head), in schedule order, kv
-// heads minor.  Each wave owns NB blocks of 32 keys and keeps dK^T and dV^T for
+// One workgroup per (sequence, key tile of BK = 256 or 128 keys, kv head), in
+// schedule order, kv heads minor.  Each wave owns NB blocks of 32 keys and keeps dK^T and dV^T for
 // them in registers (K and V sit in LDS) while the workgroup walks the 32-row
 // query tiles (from the diagonal when causal) of every query head of its GQA
 // group.  Per query tile and key block: S = Q K^T and dP = dO V^T
@@ -11,11 +11,14 @@
 // reads).  With NB > 1 a wave's operand reads of Q, dO, Q^T and dO^T serve
 // every one of its key blocks.
 //
-// LDS (bytes, DP = 128): Q and dO of two query tiles (double buffered, 32K),
-// K 64K and V 64K (resident) = 160K.  Tiles are row-major with swizzled
-// 16-byte chunks (see swz).  The next tile's Q and dO are loaded into
-// registers while the current one is computed and stored to the other buffer
-// at the end; one barrier per query tile publishes it.
+// LDS (bytes, DP = 128, BK = 256): Q and dO of two query tiles (double
+// buffered, 32K), K 64K and V 64K (resident) = 160K; the next tile's Q and dO
+// are loaded into registers while the current one is computed and stored to
+// the other buffer at the end, and one barrier per query tile publishes it.
+// BK = 128: one query tile (16K), K 32K, V 32K = 80K, two workgroups per CU;
+// the next tile is stored after a barrier that ends every wave's reads of the
+// current one, and a second barrier publishes it.  Tiles are row-major with
+// swizzled 16-byte chunks (see swz).
 #include "thd_bwd_split.hpp"
 
 namespace thd {
@@ -31,17 +34,18 @@ namespace {
 // its softmax and its waits.
 constexpr int kDkdvBlocks = 1;
 
-template <class DT, int DP, int NB>
-__global__ __launch_bounds__(512 / NB, 1) void thd_bwd_dkdv_kernel(SplitParams p) {
-  constexpr int BK = kKvBK, BQ = kKvBQ;
-  constexpr int NW = 8 / NB;        // waves per workgroup
+template <class DT, int DP, int NB, int BK>
+__global__ __launch_bounds__(64 * BK / (32 * NB), 256 * NB / BK)
+void thd_bwd_dkdv_kernel(SplitParams p) {
+  constexpr int BQ = kKvBQ, NQB = kKvQBufs<BK>;
+  constexpr int NW = BK / (32 * NB);  // waves per workgroup
   constexpr int NTH = 64 * NW;      // threads per workgroup
   constexpr int NC = DP / 16;
   constexpr int ND = DP / 32;
   constexpr int KCH = DP / 8;
   constexpr int TILE = BQ * DP * 2;
   constexpr int OFF_Q = 0;          // Q of buffer j at 2j TILE, dO at (2j + 1) TILE
-  constexpr int OFF_K = 4 * TILE;
+  constexpr int OFF_K = 2 * NQB * TILE;
   constexpr int OFF_V = OFF_K + BK * DP * 2;
   constexpr int SMEM = OFF_V + BK * DP * 2;
   constexpr int NSTAGE = (BQ * KCH + NTH - 1) / NTH;  // Q / dO chunks per thread
@@ -206,7 +210,7 @@ __global__ __launch_bounds__(512 / NB, 1) void thd_bwd_dkdv_kernel(SplitParams p
   __builtin_amdgcn_s_waitcnt(0x0f70);  // K, V blocks in LDS (not counted by the compiler)
   __syncthreads();
   for (int iter = 0; iter < n_iter; ++iter) {
-    const int qb = iter & 1;
+    const int qb = NQB == 2 ? iter & 1 : 0;
     const bool more = iter + 1 < n_iter;
     int hq_n = hq, q0_n = q0;
     advance(hq_n, q0_n);
@@ -313,10 +317,16 @@ __global__ __launch_bounds__(512 / NB, 1) void thd_bwd_dkdv_kernel(SplitParams p
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // The next tile goes into the other buffer, which every wave left at the
-    // barrier ending the previous iteration.
-    if (more) store_q(qb ^ 1);
-    __syncthreads();
+    if constexpr (NQB == 2) {
+      // The next tile goes into the other buffer, which every wave left at
+      // the barrier ending the previous iteration.
+      if (more) store_q(qb ^ 1);
+      __syncthreads();
+    } else {
+      __syncthreads();  // every wave is done with this tile's Q and dO
+      if (more) store_q(0);
+      __syncthreads();
+    }
     hq = hq_n;
     q0 = q0_n;
   }
@@ -354,8 +364,13 @@ __global__ __launch_bounds__(512 / NB, 1) void thd_bwd_dkdv_kernel(SplitParams p
 
 template <class DT, int DP>
 hipError_t launch_dkdv(const SplitParams& p, hipStream_t s) {
-  hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks>),
-                     dim3((unsigned)(p.n_ktiles * p.h_kv)), dim3(512 / kDkdvBlocks), 0, s, p);
+  const dim3 grid((unsigned)(p.n_ktiles * p.h_kv));
+  if (p.kv_bk == kKvBkLong)
+    hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkLong>), grid,
+                       dim3(64 * kKvBkLong / (32 * kDkdvBlocks)), 0, s, p);
+  else
+    hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkShort>), grid,
+                       dim3(64 * kKvBkShort / (32 * kDkdvBlocks)), 0, s, p);
   return hipGetLastError();
 }
 

@@ -58,14 +58,15 @@ struct DqSchedModel {
 // dk/dv pass schedule: key tile kt walks W = ceil(lq / BQ) query tiles, or,
 // with a causal mask type, those from the first one that sees key kt BK:
 // W = clamp(ceil(lq / BQ) - (BK / BQ) kt + ceil(off / BQ), 0, ceil(lq / BQ)).
+template <int BK>
 struct KvSchedModel {
-  static constexpr int kSlope = -kKvBK / kKvBQ;
+  static constexpr int kSlope = -BK / kKvBQ;
   const SplitParams& p;
   __device__ SeqSummary seq(int b) const {
     const int lq = split_lq(p, b), lk = split_lk(p, b);
     const int mt = mask_type_of(p.causal, b);
     SeqSummary s;
-    s.x = ceil_div_pos(lk, kKvBK);
+    s.x = ceil_div_pos(lk, BK);
     s.H = ceil_div_pos(lq, kKvBQ);
     s.causal = mask_is_causal(mt);
     s.c = s.H + ceil_div(causal_offset(mt, lq, lk), kKvBQ);
@@ -100,7 +101,7 @@ __device__ void zero_pad_rows(const int32_t* cu, const int32_t* cu_pad, int batc
   }
 }
 
-template <int DP>
+template <int DP, int BK>
 __global__ __launch_bounds__(256) void thd_bwd_split_pre_kernel(SplitParams p) {
   int blk = blockIdx.x;
   const int wave = (int)(threadIdx.x >> 6);
@@ -111,7 +112,7 @@ __global__ __launch_bounds__(256) void thd_bwd_split_pre_kernel(SplitParams p) {
   }
   blk -= p.n_qsched_wg;
   if (blk < p.n_ksched_wg) {
-    build_schedule_by_sequence(KvSchedModel{p}, p.batch, p.n_ktiles, p.ksched, blk * 4 + wave);
+    build_schedule_by_sequence(KvSchedModel<BK>{p}, p.batch, p.n_ktiles, p.ksched, blk * 4 + wave);
     return;
   }
   blk -= p.n_ksched_wg;
@@ -353,7 +354,12 @@ hipError_t launch_split_t(const SplitParams& sp, int64_t n_pre, hipStream_t s,
   hipError_t e = mark(0);
   if (e != hipSuccess) return e;
   if (n_pre > 0) {
-    hipLaunchKernelGGL((thd_bwd_split_pre_kernel<DP>), dim3((unsigned)n_pre), dim3(256), 0, s, sp);
+    if (sp.kv_bk == kKvBkLong)
+      hipLaunchKernelGGL((thd_bwd_split_pre_kernel<DP, kKvBkLong>), dim3((unsigned)n_pre), dim3(256),
+                         0, s, sp);
+    else
+      hipLaunchKernelGGL((thd_bwd_split_pre_kernel<DP, kKvBkShort>), dim3((unsigned)n_pre),
+                         dim3(256), 0, s, sp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   if ((e = mark(1)) != hipSuccess) return e;
@@ -370,7 +376,15 @@ hipError_t launch_split_t(const SplitParams& sp, int64_t n_pre, hipStream_t s,
 size_t align256_s(size_t x) { return (x + 255) & ~(size_t)255; }
 
 int64_t split_qtiles(const Problem& p) { return (p.T_q + kDqBM - 1) / kDqBM + p.batch; }
-int64_t split_ktiles(const Problem& p) { return (p.T_kv + kKvBK - 1) / kKvBK + p.batch; }
+// Keys per dk/dv workgroup, from host scalars only: a key tile walks at most
+// max_seqlen_q rows of each of the group's query heads.
+int split_kv_bk(const Problem& p) {
+  return (int64_t)p.max_q * (p.h_q / p.h_kv) <= kKvShortWalkRows ? kKvBkShort : kKvBkLong;
+}
+int64_t split_ktiles(const Problem& p) {
+  const int bk = split_kv_bk(p);
+  return (p.T_kv + bk - 1) / bk + p.batch;
+}
 
 }  // namespace
 
@@ -420,6 +434,7 @@ hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, cons
   sp.c2 = p.scale * kLog2e;
   sp.n_qtiles = (int)split_qtiles(p);
   sp.n_ktiles = (int)split_ktiles(p);
+  sp.kv_bk = split_kv_bk(p);
   const int n_sched = p.batch > 0 ? (p.batch + 3) / 4 : 0;
   sp.n_qsched_wg = n_sched;
   sp.n_ksched_wg = n_sched;

@@ -9,7 +9,18 @@ namespace thd {
 namespace split {
 
 constexpr int kDqBM = 128;   // query rows per dq workgroup (4 waves of 32 rows)
-constexpr int kKvBK = 256;   // keys per dk/dv workgroup (8 waves of 32 keys)
+// The dk/dv pass's two shapes, chosen on the host from the length of its
+// walks (max_seqlen_q times the GQA group):
+//   long walks : 256 keys (8 waves), Q and dO of two query tiles in LDS
+//                (160 KB, one workgroup per CU, one barrier per query tile);
+//   short walks: 128 keys (4 waves), one query tile in LDS (80 KB, two
+//                workgroups per CU, two barriers per query tile), so that one
+//                workgroup's K/V prologue and barriers overlap the other's work.
+constexpr int kKvBkLong = 256;
+constexpr int kKvBkShort = 128;
+constexpr int kKvShortWalkRows = 4096;  // max_seqlen_q * group up to this: short
+template <int BK>
+constexpr int kKvQBufs = BK == kKvBkLong ? 2 : 1;  // query tiles a workgroup holds in LDS
 constexpr int kKvBQ = 32;    // query rows per dk/dv step
 constexpr int kPadRows = 64; // rows per pad-zeroing workgroup
 
@@ -45,6 +56,7 @@ struct SplitParams {
   float scale, c2;   // c2 = scale * log2(e)
   int n_qtiles;      // query tiles per head (upper bound)
   int n_ktiles;      // key tiles per kv head (upper bound)
+  int kv_bk;         // keys per dk/dv workgroup: kKvBkLong or kKvBkShort
   int n_qsched_wg;   // pre-pass workgroups building the dq schedule
   int n_ksched_wg;   // ... and the dk/dv schedule
   int n_qzero_wg;    // ... zeroing pad rows of dq (kPadRows rows each)
@@ -62,7 +74,8 @@ __device__ __forceinline__ int split_lk(const SplitParams& p, int b) {
   return clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, (int64_t)p.h_kv * p.d * 2);
 }
 
-// Launch the dk/dv pass (grid n_ktiles * h_kv) on stream s.
+// Launch the dk/dv pass (grid n_ktiles * h_kv, key tiles of p.kv_bk) on
+// stream s.
 template <class DT, int DP>
 hipError_t launch_dkdv(const SplitParams& p, hipStream_t s);
 
