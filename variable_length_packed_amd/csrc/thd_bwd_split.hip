@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void thd_bwd_split_pre_kernel(SplitParams p) {
 // major with swizzled 16-byte chunks, as in the forward.
 template <class DT, int DP>
 __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
-  constexpr int BM = kDqBM, BN = DqTile<DP>::BN, NS = DqTile<DP>::NS;
+  constexpr int BM = kDqBM, BN = DqTile<DP>::BN;
   constexpr int NT = BN / 32;      // 32-key S^T tiles per LDS tile
   constexpr int NKB = BN / 16;     // 16-key blocks (K steps of dQ^T)
   constexpr int NC = DP / 16;      // 16-wide d blocks (K steps of S^T, dP^T)
@@ -150,7 +150,7 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
   static_assert(BPW >= 1 && BPW * 4096 == TILE, "tile splits into 1 KB blocks over 4 waves");
   static_assert(2 * BPW < 16, "loads of one tile fit the vmcnt field");
   // buffer j: K tile at 2j TILE, V tile at (2j + 1) TILE
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * NS * TILE];
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDqBufs * TILE];
 
   const int bid = blockIdx.x;
   const int rk = bid / p.h_q;
@@ -196,6 +196,33 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
   const char* kbase = (const char*)(p.k + sk * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d);
   const char* vbase = (const char*)(p.v + sk * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d);
 
+  uint32_t loff[BPW];
+#pragma unroll
+  for (int n = 0; n < BPW; ++n) {
+    const int slot_ = 64 * (BPW * w + n) + l;
+    const int row = slot_ / KCH;
+    const int x = slot_ - row * KCH;
+    const int gc = x ^ (int)((swz<DP>(row, 0) >> 4) & (KCH - 1));
+    loff[n] = 8 * gc < p.d ? (uint32_t)row * kvrow_bytes + 16u * gc : kOobOffset;
+  }
+  auto load_tile = [&](int k0, int buf) {
+    const uint32_t left = (uint32_t)(lk - k0);
+    const u32x4 k_rs = rsrc_words(kbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const u32x4 v_rs = rsrc_words(vbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
+    const uint32_t kt = lds_addr(smem) + (uint32_t)(2 * buf * TILE + 1024 * BPW * w);
+#pragma unroll
+    for (int n = 0; n < BPW; ++n) {
+      buf_load_lds16(k_rs, kt + 1024 * n, loff[n]);
+      buf_load_lds16(v_rs, kt + TILE + 1024 * n, loff[n]);
+    }
+  };
+  // The first tiles go in flight before the row operands are read: they
+  // need only the sequence's bounds.
+#pragma unroll
+  for (int t = 0; t < kDqBufs - 1; ++t)
+    if (t < n_kv_tiles) load_tile(t * BN, t);
+
+
   // Q and dO as the B operands of S^T and dP^T: lane holds row my_q,
   // d 16c + 8h .. +7; D = rowsum(dO * O) over the same chunks of O, the two
   // halves of a row meeting across lanes r and r + 32.
@@ -230,26 +257,6 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
 #pragma unroll
   for (int i = 0; i < ND; ++i) acc[i] = f32x16{};
 
-  uint32_t loff[BPW];
-#pragma unroll
-  for (int n = 0; n < BPW; ++n) {
-    const int slot_ = 64 * (BPW * w + n) + l;
-    const int row = slot_ / KCH;
-    const int x = slot_ - row * KCH;
-    const int gc = x ^ (int)((swz<DP>(row, 0) >> 4) & (KCH - 1));
-    loff[n] = 8 * gc < p.d ? (uint32_t)row * kvrow_bytes + 16u * gc : kOobOffset;
-  }
-  auto load_tile = [&](int k0, int buf) {
-    const uint32_t left = (uint32_t)(lk - k0);
-    const u32x4 k_rs = rsrc_words(kbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
-    const u32x4 v_rs = rsrc_words(vbase + (int64_t)k0 * kvrow_bytes, left * kvrow_bytes);
-    const uint32_t kt = lds_addr(smem) + (uint32_t)(2 * buf * TILE + 1024 * BPW * w);
-#pragma unroll
-    for (int n = 0; n < BPW; ++n) {
-      buf_load_lds16(k_rs, kt + 1024 * n, loff[n]);
-      buf_load_lds16(v_rs, kt + TILE + 1024 * n, loff[n]);
-    }
-  };
   // Operand addresses inside a tile (as in the forward):
   //   K / V rows 32tt + r, chunk 2c + h:  (b_k ^ (c << 5)) + 32tt 2DP (+ TILE for V)
   //   K^T operand (dt, kb, j):            (b_t ^ tr_chunk(dt, j)) + tr_row(kb, j)
@@ -257,76 +264,173 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
   const uint32_t b_t = swz<DP>(4 * h + (g16 >> 2), 16 * (grp & 1) + 4 * (g16 & 3));
   const float c2 = p.c2;
 
-#pragma unroll
-  for (int t = 0; t < NS - 1; ++t)
-    if (t < n_kv_tiles) load_tile(t * BN, t);
-  // vmcnt(0): operands and the first tiles are in (the tile loads are not
-  // counted by the compiler; see the forward)
-  __builtin_amdgcn_s_waitcnt(0x0f70);
-  __syncthreads();
-  int buf = 0, lbuf = NS - 1;
-  for (int it = 0; it < n_kv_tiles; ++it) {
-    const int k0 = it * BN;
-    if (it + NS - 1 < n_kv_tiles) load_tile(k0 + (NS - 1) * BN, lbuf);
+  // Tiles this wave computes: with a causal mask type, the tiles past its
+  // last row's diagonal are skipped, and so is every later tile.
+  int n_act = qw0 < lq ? n_kv_tiles : 0;
+  if (causal && n_act > 0) {
+    const int last = qw0 + 31 + off;  // last key the wave's last row sees
+    const int na = last < 0 ? 0 : last / BN + 1;
+    n_act = na < n_act ? na : n_act;
+  }
 
-    const bool active = (qw0 < lq) && (!causal || k0 <= qw0 + 31 + off);
-    if (active) {
-      const uint32_t bo = (uint32_t)(2 * buf * TILE);
-      const uint32_t a_k = opaque(b_k + bo), a_t = opaque(b_t + bo);
-      f32x16 s[NT], dp[NT];
+  // S^T and dP^T of the tile in buffer bi.
+  auto sdp = [&](int bi, f32x16 (&s)[NT], f32x16 (&dp)[NT]) {
+    const uint32_t a_k = opaque(b_k + (uint32_t)(2 * bi * TILE));
 #pragma unroll
-      for (int tt = 0; tt < NT; ++tt) {
-        s[tt] = f32x16{};
-        dp[tt] = f32x16{};
+    for (int tt = 0; tt < NT; ++tt) {
+      s[tt] = f32x16{};
+      dp[tt] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const uint32_t ad = (a_k ^ (uint32_t)(c << 5)) + 32 * tt * DP * 2;
-          const u32x4 ka = *(const u32x4*)(smem + ad);
-          const u32x4 va = *(const u32x4*)(smem + ad + TILE);
-          s[tt] = DT::mfma(as_vec8<DT>(ka), qreg[c], s[tt]);
-          dp[tt] = DT::mfma(as_vec8<DT>(va), greg[c], dp[tt]);
-        }
+      for (int c = 0; c < NC; ++c) {
+        const uint32_t ad = (a_k ^ (uint32_t)(c << 5)) + 32 * tt * DP * 2;
+        const u32x4 ka = *(const u32x4*)(smem + ad);
+        const u32x4 va = *(const u32x4*)(smem + ad + TILE);
+        s[tt] = DT::mfma(as_vec8<DT>(ka), qreg[c], s[tt]);
+        dp[tt] = DT::mfma(as_vec8<DT>(va), greg[c], dp[tt]);
       }
-      const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + off);
-      if (need_mask) {
-        const int lim = causal ? (my_q + 1 + off < lk ? my_q + 1 + off : lk) : lk;
+    }
+  };
+  // Scores of keys this lane's row does not see to -inf.
+  auto mask = [&](int k0, f32x16 (&s)[NT]) {
+    const bool need_mask = (k0 + BN > lk) || (causal && k0 + BN - 1 > qw0 + off);
+    if (need_mask) {
+      const int lim = causal ? (my_q + 1 + off < lk ? my_q + 1 + off : lk) : lk;
 #pragma unroll
-        for (int tt = 0; tt < NT; ++tt)
+      for (int tt = 0; tt < NT; ++tt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int j = k0 + 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (j >= lim) s[tt][i] = -__builtin_inff();
-          }
-      }
-      typename DT::vec8 dsb[NKB];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        float tmp[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int tt = kb >> 1, i = 8 * (kb & 1) + j;
-          const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, -lse2));
-          tmp[j] = pv * (dp[tt][i] - Drow);
-        }
-        dsb[kb] = pack8<DT>(tmp);
-      }
-#pragma unroll
-      for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-          const u32x4 a =
-              cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + tr_row<DP>(kb, 0)),
-                   lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + tr_row<DP>(kb, 1)));
-          acc[dt] = DT::mfma(as_vec8<DT>(a), dsb[kb], acc[dt]);
+        for (int i = 0; i < 16; ++i) {
+          const int j = k0 + 32 * tt + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (j >= lim) s[tt][i] = -__builtin_inff();
         }
     }
-    if (NS > 2 && it + 2 < n_kv_tiles)
-      __builtin_amdgcn_s_waitcnt(0x0f70 | (NS > 2 ? 2 * BPW : 0));
+  };
+  // dS^T of the tile in buffer bi, then dQ^T += K^T dS^T.
+  auto ds_dq = [&](int bi, const f32x16 (&s)[NT], const f32x16 (&dp)[NT]) {
+    const uint32_t a_t = opaque(b_t + (uint32_t)(2 * bi * TILE));
+    typename DT::vec8 dsb[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      float tmp[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int tt = kb >> 1, i = 8 * (kb & 1) + j;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, -lse2));
+        tmp[j] = pv * (dp[tt][i] - Drow);
+      }
+      dsb[kb] = pack8<DT>(tmp);
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 a =
+            cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + tr_row<DP>(kb, 0)),
+                 lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + tr_row<DP>(kb, 1)));
+        acc[dt] = DT::mfma(as_vec8<DT>(a), dsb[kb], acc[dt]);
+      }
+  };
+  // The next tile's S^T and dP^T (buffer bn) interleaved with this tile's
+  // dS^T (from s, dp) and then dQ^T += K^T dS^T (buffer bc).  The order is
+  // fixed by scheduling fences: segment g issues the LDS reads of a later K
+  // step, the two products of K step g and the dS of 16 / NC elements, so
+  // that the matrix unit works while the vector unit forms the
+  // probabilities.
+  auto overlapped = [&](int bc, int bn, const f32x16 (&s)[NT], const f32x16 (&dp)[NT],
+                        f32x16 (&sn)[NT], f32x16 (&dpn)[NT]) {
+    constexpr int NSEG = NT * NC;      // K steps of the next tile's products
+    constexpr int EPS = 16 * NT / NSEG;  // dS elements per segment
+    static_assert(EPS * NSEG == 16 * NT && (EPS % 2 == 0), "whole element pairs per segment");
+    const uint32_t a_k = opaque(b_k + (uint32_t)(2 * bn * TILE));
+    const uint32_t a_t = opaque(b_t + (uint32_t)(2 * bc * TILE));
+    auto kv_addr = [&](int g) {
+      return (a_k ^ (uint32_t)((g % NC) << 5)) + 32 * (g / NC) * DP * 2;
+    };
+#pragma unroll
+    for (int tt = 0; tt < NT; ++tt) {
+      sn[tt] = f32x16{};
+      dpn[tt] = f32x16{};
+    }
+    float tmp[16 * NT];
+    typename DT::vec8 dsb[NKB];
+    // LDS reads run kDqReadAhead K steps ahead of their products
+    constexpr int RA = kDqReadAhead < NSEG ? kDqReadAhead : NSEG;
+    u32x4 kr[RA + 1], vr[RA + 1];
+#pragma unroll
+    for (int g = 0; g < RA; ++g) {
+      kr[g] = *(const u32x4*)(smem + kv_addr(g));
+      vr[g] = *(const u32x4*)(smem + kv_addr(g) + TILE);
+    }
+#pragma unroll
+    for (int g = 0; g < NSEG; ++g) {
+      if (g + RA < NSEG) {
+        kr[(g + RA) % (RA + 1)] = *(const u32x4*)(smem + kv_addr(g + RA));
+        vr[(g + RA) % (RA + 1)] = *(const u32x4*)(smem + kv_addr(g + RA) + TILE);
+      }
+      const u32x4 ka = kr[g % (RA + 1)], va = vr[g % (RA + 1)];
+      const int tt = g / NC, c = g % NC;
+      sn[tt] = DT::mfma(as_vec8<DT>(ka), qreg[c], sn[tt]);
+      dpn[tt] = DT::mfma(as_vec8<DT>(va), greg[c], dpn[tt]);
+#pragma unroll
+      for (int e = 0; e < EPS; ++e) {
+        const int x = g * EPS + e;
+        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[x >> 4][x & 15], c2, -lse2));
+        tmp[x] = pv * (dp[x >> 4][x & 15] - Drow);
+        // pins the element's vector work to this segment (instruction
+        // selection would otherwise move it next to its use)
+        asm volatile("" : "+v"(tmp[x]));
+      }
+      if (((g + 1) * EPS) % 8 == 0) {
+        const int kb = ((g + 1) * EPS) / 8 - 1;
+        dsb[kb] = pack8<DT>(tmp + 8 * kb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 a =
+            cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + tr_row<DP>(kb, 0)),
+                 lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + tr_row<DP>(kb, 1)));
+        acc[dt] = DT::mfma(as_vec8<DT>(a), dsb[kb], acc[dt]);
+      }
+  };
+  // Iteration it: tiles it and it + 1 are in LDS (buffers it % B and
+  // (it + 1) % B, B = kDqBufs), tile it + 2 is in flight, and tile it + B - 1
+  // is loaded into the buffer tile it - 1 used.
+  // S^T and dP^T of tile it + 1 are formed while the probabilities and dS of
+  // tile it are (the two are independent, so the matrix products overlap the
+  // vector work); the scores of tile it arrive in (s, dp) from the iteration
+  // before.
+  auto step = [&](int it, f32x16 (&s)[NT], f32x16 (&dp)[NT], f32x16 (&sn)[NT],
+                  f32x16 (&dpn)[NT]) {
+    if (it + kDqBufs - 1 < n_kv_tiles)
+      load_tile((it + kDqBufs - 1) * BN, (it + kDqBufs - 1) % kDqBufs);
+    if (it < n_act) {
+      // (the products of the next tile are formed even past this wave's last
+      // tile: its buffer is in LDS either way, and a branch would split the
+      // block in which they overlap this tile's vector work)
+      mask(it * BN, s);
+      overlapped(it % kDqBufs, (it + 1) % kDqBufs, s, dp, sn, dpn);
+    }
+    // Tile it + 2 is in; the one loaded after it (2 BPW loads) may still be
+    // in flight.  (The tile loads are not counted by the compiler; see the
+    // forward.)
+    if (kDqBufs > 3 && it + 3 < n_kv_tiles)
+      __builtin_amdgcn_s_waitcnt(0x0f70 | (kDqBufs > 3 ? 2 * BPW : 0));
     else
       __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
-    buf = buf + 1 == NS ? 0 : buf + 1;
-    lbuf = lbuf + 1 == NS ? 0 : lbuf + 1;
+  };
+
+  // vmcnt(0): operands and the first tiles are in
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  f32x16 s0[NT], dp0[NT], s1[NT], dp1[NT];
+  if (n_act > 0) sdp(0, s0, dp0);
+  for (int it = 0; it < n_kv_tiles; it += 2) {
+    step(it, s0, dp0, s1, dp1);
+    if (it + 1 < n_kv_tiles) step(it + 1, s1, dp1, s0, dp0);
   }
 
   // dq = scale dQ; rows past lq are dropped by the resource bound.

@@ -25,12 +25,13 @@ constexpr int kKvBQ = 32;    // query rows per dk/dv step
 constexpr int kPadRows = 64; // rows per pad-zeroing workgroup
 
 // Key tiles of the dq pass: as the forward's (32 keys at d > 32, 64 at
-// d <= 32), double buffered at d = 128.
+// d <= 32); three buffers, two tiles resident and one loading.
 template <int DP>
 struct DqTile {
   static constexpr int BN = DP > 32 ? 32 : 64;
-  static constexpr int NS = DP == 64 ? 3 : 2;
 };
+constexpr int kDqBufs = 3;
+constexpr int kDqReadAhead = 1;  // K steps between an LDS read and its product
 
 struct SplitParams {
   const uint16_t* q;
