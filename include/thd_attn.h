@@ -34,10 +34,10 @@
  *   - Size limits (THD_ERR_SHAPE otherwise): total_q, total_kv < 2^31; a
  *     sequence's rows are addressed with 32-bit byte offsets, so
  *     max_seqlen_q * h_q * head_dim * 2 and max_seqlen_kv * h_kv * head_dim * 2
- *     must be below 2^31, and for the backward also
- *     max_seqlen_q * h_q * DP * 4 (its fp32 dq accumulator; DP = head_dim
- *     rounded up to 32, 64, 128 or 256) and total_q * h_q / 32.  max_seqlen_* must
- *     bound the true lengths: a longer sequence is clamped as above.
+ *     must be below 2^31, and for the backward above head_dim 128 also
+ *     max_seqlen_q * h_q * 256 * 4 (its fp32 dq accumulator) and
+ *     total_q * h_q / 32.  max_seqlen_* must bound the true lengths: a longer
+ *     sequence is clamped as above.
  *   - No C++ exception crosses this interface.
  *
  * Sequence placement [I], [C]

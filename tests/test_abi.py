@@ -76,8 +76,8 @@ def test_fwd_rejects_invalid_arguments(kw, status):
 
 def test_sequence_size_limits():
     # 32-bit byte offsets per sequence: q / k / v rows of max_seqlen rows must
-    # stay below 2^31 bytes, and in the backward the fp32 dq accumulator rows
-    # (h_q * DP * 4 bytes) too.
+    # stay below 2^31 bytes, and in the backward above head dim 128 the fp32
+    # dq accumulator rows (h_q * 256 * 4 bytes) too.
     lib = _lib.load()
     fwd = lambda a: lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, P, 1 << 30, None)
     bwd = lambda a: lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, 1 << 30, None)
@@ -85,14 +85,20 @@ def test_sequence_size_limits():
     assert fwd(_args(**big_q)) == -2 and bwd(_args(**big_q)) == -2
     big_kv = dict(max_seqlen_kv=(1 << 31) // (2 * 64 * 2), total_kv=1 << 21)
     assert fwd(_args(**big_kv)) == -2 and bwd(_args(**big_kv)) == -2
-    # fits the forward's bf16 rows but not the backward's fp32 accumulator
-    acc_only = dict(max_seqlen_q=(1 << 31) // (4 * 64 * 4), total_q=1 << 20)
+    # fits the 16-bit rows of d = 256 but not the backward's fp32 accumulator
+    acc_only = dict(max_seqlen_q=(1 << 31) // (4 * 256 * 4), total_q=1 << 20, head_dim=256)
     assert bwd(_args(**acc_only)) == -2
     assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**acc_only))) == 0
     # the forward passes the size checks and stops at the (empty) workspace,
     # before anything could be launched with the placeholder pointers
     assert lib.thd_attn_fwd(ctypes.byref(_args(**acc_only)), P, P, P, P, P, P, 0, None) == -4
     assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(**acc_only))) > 0
+    # up to head dim 128 the backward has no accumulator: the same rows at
+    # d = 128 pass its size checks and stop at the (empty) workspace
+    no_acc = dict(max_seqlen_q=(1 << 31) // (4 * 256 * 4), total_q=1 << 20, head_dim=128)
+    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**no_acc))) > 0
+    assert lib.thd_attn_bwd(ctypes.byref(_args(**no_acc)), P, P, P, P, P, P, P, P, P, P, 0,
+                            None) == -4
 
 
 def test_null_and_misaligned_tensors():

@@ -21,18 +21,18 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // Kernels address a sequence's rows with 32-bit byte offsets from its first
 // row, so max_seqlen rows of every buffer they address per sequence must
-// stay below 2^31 bytes: q / o rows (h_q * head_dim * 2 bytes), k / v rows
-// (h_kv * head_dim * 2) and, in the backward, the fp32 dq accumulator rows
-// (h_q * DP * 4, DP = head_dim rounded up to 32, 64, 128 or 256).  The backward's
-// pre and post passes take one workgroup per 32 (row, head) pairs.
+// stay below 2^31 bytes: q / o / dq rows (h_q * head_dim * 2 bytes), k / v
+// rows (h_kv * head_dim * 2) and, in the backward above head dim 128, the
+// fp32 dq accumulator rows (h_q * 256 * 4), whose pre and post passes also
+// take one workgroup per 32 (row, head) pairs.
 int check_sizes(const thd_varlen_args* a, bool backward) {
   const int64_t lim = (int64_t)1 << 31;
-  const int dp = a->head_dim <= 32 ? 32 : a->head_dim <= 64 ? 64 : a->head_dim <= 128 ? 128 : 256;
-  const int64_t q_row = (int64_t)a->h_q * (backward ? dp * 4 : a->head_dim * 2);
+  const bool acc = backward && a->head_dim > 128;
+  const int64_t q_row = (int64_t)a->h_q * (acc ? 256 * 4 : a->head_dim * 2);
   const int64_t kv_row = (int64_t)a->h_kv * a->head_dim * 2;
   if ((int64_t)a->max_seqlen_q * q_row >= lim || (int64_t)a->max_seqlen_kv * kv_row >= lim)
     return THD_ERR_SHAPE;
-  if (backward && a->total_q * a->h_q / 32 >= lim) return THD_ERR_SHAPE;
+  if (acc && a->total_q * a->h_q / 32 >= lim) return THD_ERR_SHAPE;
   return THD_OK;
 }
 
