@@ -148,7 +148,7 @@ def test_workspace_size_and_check():
     # two fp32 row statistics [h_q, T_q], the dq pass's schedule of query
     # tiles and the dk/dv pass's of key tiles (no fp32 dq accumulator at
     # head dims up to 128); above 128, also the fp32 dq accumulator
-    assert need >= 2 * 16 * 4 * 4 + 2 * (2 + 2 * (1 + 2)) * 4
+    assert need >= 2 * 16 * 4 * 4 + 2 * (8 + 8 * (1 + 2)) * 4
     wide = lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(head_dim=192)))
     assert wide >= 16 * 4 * 256 * 4 + 2 * 16 * 4 * 4
     assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(batch=-1))) == 0

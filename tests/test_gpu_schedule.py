@@ -12,8 +12,9 @@ sequences by their largest item's work, largest first, ties in sequence
 order; within a sequence, its items largest first.  Workspace layouts (sizes
 from the library's own size queries): forward = the schedule; backward =
 -D and -LSE/scale [2][h_q][T_q], then the dq pass's schedule, then the dk/dv
-pass's, each part starting on a 256-byte boundary.  Schedule = int32 [count,
-unused, (b, t) per rank].
+pass's, each part starting on a 256-byte boundary.  Schedule = int32
+[count, 7 unused, then per rank 8 words: b, t, the sequence's query and key
+slot starts, its query and key lengths, its mask type, unused].
 Bit-exact comparison: the schedule is integer work.
 """
 import numpy as np
@@ -62,10 +63,21 @@ def expected_schedule(lens_items, lens_walk, types, per_item, per_walk, slope):
     return out
 
 
-def read_schedule(ws, offset):
+HEADER, WORDS = 8, 8   # int32 words before the first item, and per item
+
+
+def read_schedule(ws, offset, w=None, types=None):
+    """(b, t) per rank.  With the workload, also checks each item's other
+    fields: the sequence's slot starts, lengths and mask type."""
     a = ws[offset:].view(torch.int32).cpu().numpy()
     n = int(a[0])
-    return [(int(a[2 + 2 * r]), int(a[3 + 2 * r])) for r in range(n)]
+    items = a[HEADER:HEADER + WORDS * n].reshape(n, WORDS) if n else np.zeros((0, WORDS), int)
+    if w is not None:
+        sq, sk = w.starts_q(), w.starts_kv()
+        for rank, (b, t, s_q, s_k, l_q, l_k, mt, _) in enumerate(items.tolist()):
+            assert (s_q, s_k, l_q, l_k, mt) == (int(sq[b]), int(sk[b]), int(w.lens_q[b]),
+                                                int(w.lens_kv[b]), int(types[b])), rank
+    return [(int(b), int(t)) for b, t in items[:, :2].tolist()]
 
 
 def align256(x):
@@ -102,7 +114,7 @@ def test_schedules_match_definition(kw):
     torch.cuda.synchronize()
     bn = 32 if w.d > 32 else 64
     exp_f = expected_schedule(w.lens_q, w.lens_kv, types, 128, bn, 128 // bn)
-    assert read_schedule(ws, 0) == exp_f
+    assert read_schedule(ws, 0, w, types) == exp_f
 
     need_b = thd.bwd_workspace_size(q, k, meta["cu_seqlens_q"], meta["cu_seqlens_kv"],
                                     batch_size=w.batch)
@@ -115,10 +127,10 @@ def test_schedules_match_definition(kw):
     torch.cuda.synchronize()
     off_q = align256(w.T_q * w.h_q * 2 * 4)
     n_qtiles = ceil_div(w.T_q, 128) + w.batch   # the dq pass's query-tile bound
-    off_k = off_q + align256((2 + 2 * n_qtiles) * 4)
-    assert read_schedule(ws_b, off_q) == exp_f
+    off_k = off_q + align256((HEADER + WORDS * n_qtiles) * 4)
+    assert read_schedule(ws_b, off_q, w, types) == exp_f
     # key tiles of the dk/dv pass: 128 keys when max_seqlen_q times the GQA
     # group is at most 4096, else 256
     bk = 128 if w.max_seqlen_q * (w.h_q // w.h_kv) <= 4096 else 256
     exp_b = expected_schedule(w.lens_kv, w.lens_q, types, bk, 32, -(bk // 32))
-    assert read_schedule(ws_b, off_k) == exp_b
+    assert read_schedule(ws_b, off_k, w, types) == exp_b

@@ -45,7 +45,7 @@ struct BwdParams {
   float* dq_acc;  // [T_q, h_q, DP], row-major like dq
   float* dsum;    // [h_q, T_q], holds -D
   float* lsum;    // [h_q, T_q], holds -LSE / scale
-  int32_t* sched; // [2 + 2 * n_kv_tiles]: item count, then (sequence, key tile) by rank
+  int32_t* sched; // item count, then the items by rank (build_schedule_by_sequence)
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const int32_t* pad_q;
@@ -88,6 +88,11 @@ struct BwdSchedModel {
     s.H = ceil_div_pos(lq, kBwdBQ);
     s.causal = mask_is_causal(mt);
     s.c = s.H + ceil_div(causal_offset(mt, lq, lk), kBwdBQ);
+    s.sq = (int)sq;
+    s.sk = (int)sk;
+    s.lq = lq;
+    s.lk = lk;
+    s.mtype = mt;
     return s;
   }
 };
@@ -203,9 +208,10 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_wide_kernel(BwdParams p) 
   const int bid = blockIdx.x;
   const int rk = bid / p.h_kv;
   const int hk = bid - rk * p.h_kv;
-  if (rk >= p.sched[0]) return;
-  const int b = uniform(p.sched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
+  SchedItem item;
+  if (!load_sched_item(p.sched, rk, item)) return;
+  const int b = uniform(item.b);
+  const int tile_in_seq = uniform(item.t);
   if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
@@ -221,11 +227,13 @@ __global__ __launch_bounds__(256, 1) void thd_bwd_main_wide_kernel(BwdParams p) 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
   const uint32_t accrow_bytes = (uint32_t)p.h_q * DP * 4;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, accrow_bytes));
-  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const int mtype = mask_type_of(p.causal, b);
+  // the item's slot starts, lengths (clamped as BwdSchedModel clamps them)
+  // and mask type
+  const int64_t sq = uniform(item.sq);
+  const int64_t sk = uniform(item.sk);
+  const int lq = uniform(item.lq);
+  const int lk = uniform(item.lk);
+  const int mtype = uniform(item.mtype);
   const bool causal = mask_is_causal(mtype);
   const int off = causal_offset(mtype, lq, lk);
   const int k0 = tile_in_seq * BK;
@@ -561,14 +569,14 @@ static int64_t kv_tile_bound(const Problem& p) { return (p.T_kv + kWideBK - 1) /
 
 // Head dims up to 128: the two-pass backward's workspace.  Above: the fp32 dq
 // accumulator [T_q][h_q][256], then -D = -rowsum(dO * O) and -LSE / scale (each [h_q][T_q]), then
-// the main kernel's schedule (2 + 2 * key-tile bound int32).
+// the main kernel's schedule (sched_bytes of the key-tile bound).
 static bool use_split(const Problem& p) { return p.d <= 128; }
 
 size_t bwd_workspace_bytes(const Problem& p) {
   if (use_split(p)) return split_bwd_workspace_bytes(p);
   const size_t acc = align256((size_t)p.T_q * p.h_q * padded_dim(p.d) * sizeof(float));
   const size_t dsum = align256((size_t)p.T_q * p.h_q * 2 * sizeof(float));
-  const size_t sched = align256((size_t)(2 + 2 * kv_tile_bound(p)) * sizeof(int32_t));
+  const size_t sched = align256(sched_bytes(kv_tile_bound(p)));
   return acc + dsum + sched;
 }
 

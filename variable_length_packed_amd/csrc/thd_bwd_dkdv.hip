@@ -59,9 +59,10 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
   const int bid = blockIdx.x;
   const int rk = bid / p.h_kv;
   const int hk = bid - rk * p.h_kv;
-  if (rk >= p.ksched[0]) return;
-  const int b = uniform(p.ksched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.ksched[3 + 2 * rk]);
+  SchedItem item;
+  if (!load_sched_item(p.ksched, rk, item)) return;
+  const int b = uniform(item.b);
+  const int tile_in_seq = uniform(item.t);
   if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
@@ -74,11 +75,12 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(split_lq(p, b));
-  const int lk = uniform(split_lk(p, b));
-  const int mtype = mask_type_of(p.causal, b);
+  // the item's slot starts, lengths (split_lq / split_lk) and mask type
+  const int64_t sq = uniform(item.sq);
+  const int64_t sk = uniform(item.sk);
+  const int lq = uniform(item.lq);
+  const int lk = uniform(item.lk);
+  const int mtype = uniform(item.mtype);
   const bool causal = mask_is_causal(mtype);
   const int off = causal_offset(mtype, lq, lk);
   const int k0 = tile_in_seq * BK;

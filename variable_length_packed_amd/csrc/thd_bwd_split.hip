@@ -51,6 +51,11 @@ struct DqSchedModel {
     s.H = ceil_div_pos(lk, BN);
     s.causal = mask_is_causal(mt);
     s.c = kSlope + ceil_div(causal_offset(mt, lq, lk), BN);
+    s.sq = (int)seq_start(p.cu_q, p.pad_q, b);
+    s.sk = (int)seq_start(p.cu_kv, p.pad_kv, b);
+    s.lq = lq;
+    s.lk = lk;
+    s.mtype = mt;
     return s;
   }
 };
@@ -70,6 +75,11 @@ struct KvSchedModel {
     s.H = ceil_div_pos(lq, kKvBQ);
     s.causal = mask_is_causal(mt);
     s.c = s.H + ceil_div(causal_offset(mt, lq, lk), kKvBQ);
+    s.sq = (int)seq_start(p.cu_q, p.pad_q, b);
+    s.sk = (int)seq_start(p.cu_kv, p.pad_kv, b);
+    s.lq = lq;
+    s.lk = lk;
+    s.mtype = mt;
     return s;
   }
 };
@@ -156,9 +166,10 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
   const int rk = bid / p.h_q;
   const int slot = bid - rk * p.h_q;
   const int hq = (slot % p.h_kv) * p.group + slot / p.h_kv;
-  if (rk >= p.qsched[0]) return;
-  const int b = uniform(p.qsched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.qsched[3 + 2 * rk]);
+  SchedItem item;
+  if (!load_sched_item(p.qsched, rk, item)) return;
+  const int b = uniform(item.b);
+  const int tile_in_seq = uniform(item.t);
   if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
@@ -171,11 +182,12 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(split_lq(p, b));
-  const int lk = uniform(split_lk(p, b));
-  const int mtype = mask_type_of(p.causal, b);
+  // the item's slot starts, lengths (split_lq / split_lk) and mask type
+  const int64_t sq = uniform(item.sq);
+  const int64_t sk = uniform(item.sk);
+  const int lq = uniform(item.lq);
+  const int lk = uniform(item.lk);
+  const int mtype = uniform(item.mtype);
   const bool causal = mask_is_causal(mtype);
   const int off = causal_offset(mtype, lq, lk);
   const int hk = hq / p.group;
@@ -493,12 +505,12 @@ int64_t split_ktiles(const Problem& p) {
 }  // namespace
 
 // -D and -LSE/scale ([h_q][T_q] fp32 each), then the dq pass's schedule
-// (2 + 2 * query-tile bound int32) and the dk/dv pass's (2 + 2 * key-tile
-// bound int32).
+// (sched_bytes of the query-tile bound) and the dk/dv pass's (of the
+// key-tile bound).
 size_t split_bwd_workspace_bytes(const Problem& p) {
   const size_t stats = align256_s((size_t)p.T_q * p.h_q * 2 * sizeof(float));
-  const size_t qs = align256_s((size_t)(2 + 2 * split_qtiles(p)) * sizeof(int32_t));
-  const size_t ks = align256_s((size_t)(2 + 2 * split_ktiles(p)) * sizeof(int32_t));
+  const size_t qs = align256_s(sched_bytes(split_qtiles(p)));
+  const size_t ks = align256_s(sched_bytes(split_ktiles(p)));
   return stats + qs + ks;
 }
 
@@ -521,7 +533,7 @@ hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, cons
   sp.lsum = sp.dsum + (size_t)p.T_q * p.h_q;
   sp.qsched = (int32_t*)((char*)workspace + stats);
   sp.ksched = (int32_t*)((char*)workspace + stats +
-                         align256_s((size_t)(2 + 2 * split_qtiles(p)) * sizeof(int32_t)));
+                         align256_s(sched_bytes(split_qtiles(p))));
   sp.cu_q = p.cu_q;
   sp.cu_kv = p.cu_kv;
   sp.pad_q = p.pad_q;

@@ -45,8 +45,8 @@ struct SplitParams {
   uint16_t* dv;
   float* dsum;      // [h_q, T_q]: -D, written by the dq pass
   float* lsum;      // [h_q, T_q]: -LSE / scale, written by the dq pass
-  int32_t* qsched;  // [2 + 2 n_qtiles]: item count, then (sequence, query tile) by rank
-  int32_t* ksched;  // [2 + 2 n_ktiles]: item count, then (sequence, key tile) by rank
+  int32_t* qsched;  // item count, then (sequence, query tile) items by rank
+  int32_t* ksched;  // item count, then (sequence, key tile) items by rank
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const int32_t* pad_q;

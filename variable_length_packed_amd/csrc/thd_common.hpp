@@ -348,16 +348,51 @@ __device__ __forceinline__ int clampi(int x, int lo, int hi) { return x < lo ? l
 // and short ones fill in behind them, and every tile of a sequence and head
 // runs at about the same time on the XCD that the head fixes, so tiles that
 // walk the same rows of the other operand share them in L2.
-// Output: sched[0] = number of tiles kept (at most cap), then (b, t) of rank
-// r at sched[2 + 2r], sched[3 + 2r].  One wave per sequence (wave_id = b);
-// its lanes take t = lane, lane + 64, ...; the wave of sequence 0 also
-// writes sched[0].
+// Output: sched[0] = number of tiles kept (at most cap); the item of rank r
+// at sched + kSchedHeader + kSchedWords r: the tile and everything its
+// workgroup needs to start (sequence, tile, slot starts, clamped lengths,
+// mask type), so that the workgroup reads one 32-byte record and no
+// sequence metadata.  One wave per sequence (wave_id = b); its lanes take
+// t = lane, lane + 64, ...; the wave of sequence 0 also writes sched[0].
 // ---------------------------------------------------------------------------
 struct SeqSummary {
   int x;        // tiles of the sequence
   int c, H;     // W(t) = clamp(a t + c, 0, H) when causal, else H; H < 2^30
   bool causal;
+  int sq, sk;   // first rows of the sequence's query and key slots
+  int lq, lk;   // lengths as the pass's kernel clamps them
+  int mtype;    // mask type
 };
+
+constexpr int kSchedHeader = 8;  // int32 words before the first item
+constexpr int kSchedWords = 8;   // int32 words per item
+struct SchedItem {
+  int32_t b, t;     // sequence, tile within it
+  int32_t sq, sk;   // first rows of its query and key slots
+  int32_t lq, lk;   // clamped lengths
+  int32_t mtype;    // mask type
+  int32_t unused;
+};
+static_assert(sizeof(SchedItem) == 4 * kSchedWords, "one item per kSchedWords words");
+
+// Bytes of a schedule of at most cap items.
+inline size_t sched_bytes(int64_t cap) {
+  return (size_t)(kSchedHeader + kSchedWords * cap) * sizeof(int32_t);
+}
+
+// The item of `rank` (rank < the schedule's capacity, so the read stays in
+// the buffer) and whether the schedule kept it: the count and the item are
+// loaded together, one round trip.  The item of a rank past the count is
+// stale and must not be used.
+__device__ __forceinline__ bool load_sched_item(const int32_t* sched, int rank, SchedItem& it) {
+  const int n = sched[0];
+  it = *(const SchedItem*)(sched + kSchedHeader + kSchedWords * rank);
+  // Uses the item before the count is tested: without it the compiler sinks
+  // the item's loads below that branch, one round trip each.
+  asm volatile("" ::"s"(it.b), "s"(it.t), "s"(it.sq), "s"(it.sk), "s"(it.lq), "s"(it.lk),
+               "s"(it.mtype));
+  return rank < n;
+}
 
 // Work of a sequence's largest tile (-1 for a sequence without tiles).
 template <class Model>
@@ -397,10 +432,18 @@ __device__ void build_schedule_by_sequence(const Model& md, int batch, int cap, 
   for (int t = lane; t < sb.x; t += 64) {
     const int rank = before + (descending ? sb.x - 1 - t : t);
     if (rank < cap) {
-      int2 e;
-      e.x = b;
-      e.y = t;
-      *(int2*)(sched + 2 + 2 * rank) = e;
+      int4 e0, e1;
+      e0.x = b;
+      e0.y = t;
+      e0.z = sb.sq;
+      e0.w = sb.sk;
+      e1.x = sb.lq;
+      e1.y = sb.lk;
+      e1.z = sb.mtype;
+      e1.w = 0;
+      int4* dst = (int4*)(sched + kSchedHeader + kSchedWords * rank);
+      dst[0] = e0;
+      dst[1] = e1;
     }
   }
   if (b == 0 && lane == 0) sched[0] = min(total, cap);

@@ -66,7 +66,7 @@ struct FwdParams {
   int n_tiles;      // query tiles per head (upper bound over all layouts)
   int n_attn;       // n_tiles * h_q workgroups doing attention
   int n_sched;      // workgroups of the pre pass building the schedule
-  int32_t* sched;   // [2 + 2 * n_tiles]: item count, then (sequence, tile) by rank
+  int32_t* sched;   // item count, then the items by rank (build_schedule_by_sequence)
 };
 
 // Schedule of the attention workgroups (grouped by sequence, largest tile
@@ -93,6 +93,11 @@ struct FwdSchedModel {
     s.H = ceil_div_pos(lk, BN);
     s.causal = mask_is_causal(mt);
     s.c = kSlope + ceil_div(causal_offset(mt, lq, lk), BN);
+    s.sq = (int)sq;
+    s.sk = (int)sk;
+    s.lq = lq;
+    s.lk = lk;
+    s.mtype = mt;
     return s;
   }
 };
@@ -166,9 +171,10 @@ __global__ __launch_bounds__(256, FwdTile<DP>::WG_PER_CU) void thd_fwd_kernel(Fw
   const int rk = bid / p.h_q;
   const int slot = bid - rk * p.h_q;
   const int hq = (slot % p.h_kv) * p.group + slot / p.h_kv;
-  if (rk >= p.sched[0]) return;
-  const int b = uniform(p.sched[2 + 2 * rk]);
-  const int tile_in_seq = uniform(p.sched[3 + 2 * rk]);
+  SchedItem item;
+  if (!load_sched_item(p.sched, rk, item)) return;
+  const int b = uniform(item.b);
+  const int tile_in_seq = uniform(item.t);
   if (b < 0 || b >= p.batch || tile_in_seq < 0) return;
 
   const int tid = threadIdx.x;
@@ -181,11 +187,13 @@ __global__ __launch_bounds__(256, FwdTile<DP>::WG_PER_CU) void thd_fwd_kernel(Fw
 
   const uint32_t qrow_bytes = (uint32_t)p.h_q * p.d * 2;
   const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
-  const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
-  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
-  const int lq = uniform(clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, qrow_bytes));
-  const int lk = uniform(clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes));
-  const int mtype = mask_type_of(p.causal, b);
+  // the item's slot starts, lengths (clamped as FwdSchedModel clamps them)
+  // and mask type
+  const int64_t sq = uniform(item.sq);
+  const int64_t sk = uniform(item.sk);
+  const int lq = uniform(item.lq);
+  const int lk = uniform(item.lk);
+  const int mtype = uniform(item.mtype);
   const bool causal = mask_is_causal(mtype);
   const int off = causal_offset(mtype, lq, lk);  // key j visible to query i iff j <= i + off
   const int hk = hq / p.group;
@@ -404,11 +412,11 @@ int64_t fwd_tile_bound(const Problem& p) { return (p.T_q + kFwdBM - 1) / kFwdBM 
 
 }  // namespace
 
-// The attention workgroups' schedule: 2 + 2 * query-tile bound int32; or,
+// The attention workgroups' schedule (sched_bytes of the query-tile bound); or,
 // for few query rows per sequence, the split-KV partials.
 size_t fwd_workspace_bytes(const Problem& p) {
   if (decode_applies(p)) return decode_workspace_bytes(p);
-  return p.batch > 0 ? (size_t)(2 + 2 * fwd_tile_bound(p)) * sizeof(int32_t) : 0;
+  return p.batch > 0 ? sched_bytes(fwd_tile_bound(p)) : 0;
 }
 
 static FwdParams pad_params(const Problem& p, void* o, float* lse) {
