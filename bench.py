@@ -72,7 +72,8 @@ def source_digest(kernel):
     import hashlib
     from variable_length_packed_amd.build import compile_flags
     h = hashlib.sha256()
-    h.update(" ".join(f for f in compile_flags() if not f.startswith("-I")).encode())
+    flags = compile_flags(KERNEL_SOURCES[kernel][0])
+    h.update(" ".join(f for f in flags if not f.startswith("-I")).encode())
     for name in KERNEL_SOURCES[kernel]:
         h.update(name.encode())
         with open(os.path.join(ROOT, "variable_length_packed_amd", "csrc", name), "rb") as f:

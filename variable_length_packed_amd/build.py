@@ -27,8 +27,17 @@ def hipcc_path():
     raise RuntimeError("hipcc not found; ROCm is required to build libthdattn.so")
 
 
+# Per-source scheduler choice: the latency-oriented machine scheduler ran
+# the forward and the dq pass 1-2 % faster on 16 causal sequences of 64-2048
+# tokens (h = 16, d = 128) and the dk/dv pass no faster.
+PER_SOURCE_FLAGS = {
+    "thd_fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+    "thd_bwd_split.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+}
+
+
 def compile_flags(source=None):
-    """hipcc flags for one source (all of them when source is None)."""
+    """hipcc flags for one source (the common ones when source is None)."""
     flags = [
         f"--offload-arch={ARCH}",
         "-O3",
@@ -44,6 +53,8 @@ def compile_flags(source=None):
     # MFMA results in VGPRs: the softmax / gradient VALU work reads them
     # directly instead of copying them out of AGPRs
     flags += ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+    if source is not None:
+        flags += PER_SOURCE_FLAGS.get(os.path.basename(source), [])
     return flags
 
 
