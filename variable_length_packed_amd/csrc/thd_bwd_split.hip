@@ -9,10 +9,12 @@
 //               dQ = scale dS K in registers; it also forms D = rowsum(dO * O)
 //               from the stored output and leaves -D and -LSE/scale for
 //               the second pass;
-//   dk/dv pass: key-stationary: one workgroup of 8 waves per (sequence,
-//               256-key tile, kv head) walks the 32-row query tiles of every
-//               query head of its GQA group, recomputes S and dP and
-//               accumulates dK^T and dV^T in registers.
+//   dk/dv pass: key-stationary: one workgroup per (sequence, key tile, kv
+//               head), 32 keys per wave (128-key tiles of 4 waves for short
+//               walks, 256-key tiles of 8 waves for long ones), walks the
+//               32-row query tiles of every query head of its GQA group,
+//               recomputes S and dP and accumulates dK^T and dV^T in
+//               registers (thd_bwd_dkdv.hip).
 // Textbook softmax-attention backward with the probabilities recomputed from
 // the forward's log-sum-exp:
 //   P = exp(scale Q K^T - LSE),  dV = P^T dO,  dP = dO V^T,
@@ -315,31 +317,6 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
           if (j >= lim) s[tt][i] = -__builtin_inff();
         }
     }
-  };
-  // dS^T of the tile in buffer bi, then dQ^T += K^T dS^T.
-  auto ds_dq = [&](int bi, const f32x16 (&s)[NT], const f32x16 (&dp)[NT]) {
-    const uint32_t a_t = opaque(b_t + (uint32_t)(2 * bi * TILE));
-    typename DT::vec8 dsb[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      float tmp[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int tt = kb >> 1, i = 8 * (kb & 1) + j;
-        const float pv = __builtin_amdgcn_exp2f(__builtin_fmaf(s[tt][i], c2, -lse2));
-        tmp[j] = pv * (dp[tt][i] - Drow);
-      }
-      dsb[kb] = pack8<DT>(tmp);
-    }
-#pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const u32x4 a =
-            cat2(lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 0)) + tr_row<DP>(kb, 0)),
-                 lds_read_tr(smem, (a_t ^ tr_chunk<DP>(dt, 1)) + tr_row<DP>(kb, 1)));
-        acc[dt] = DT::mfma(as_vec8<DT>(a), dsb[kb], acc[dt]);
-      }
   };
   // The next tile's S^T and dP^T (buffer bn) interleaved with this tile's
   // dS^T (from s, dp) and then dQ^T += K^T dS^T (buffer bc).  The order is
