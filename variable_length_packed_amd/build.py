@@ -101,6 +101,43 @@ def build_library(verbose=False, extra_flags=()):
     return LIB_PATH
 
 
+def asan_runtime():
+    """Path of the clang AddressSanitizer runtime that hipcc's host pass links
+    against, or None."""
+    root = os.path.dirname(os.path.dirname(os.path.realpath(hipcc_path())))
+    cands = sorted(glob.glob(os.path.join(root, "llvm", "lib", "clang", "*", "lib", "linux",
+                                          "libclang_rt.asan-x86_64.so")))
+    return cands[-1] if cands else None
+
+
+def build_host_asan_library(out_path):
+    """A copy of the library whose host code in thd_api.hip (argument checks,
+    workspace sizes, status strings) is built with AddressSanitizer; the
+    other sources' objects come from the last build_library run.  Device code
+    is built as usual: the sanitizer flags are host-only."""
+    objdir = os.path.join(PKG_DIR, "_build")
+    others = [o for o in sorted(glob.glob(os.path.join(objdir, "*.hip.o")))
+              if os.path.basename(o) != "thd_api.hip.o"]
+    if not others:
+        raise RuntimeError("build_library() first: its objects are linked in")
+    hipcc = hipcc_path()
+    src = os.path.join(CSRC, "thd_api.hip")
+    obj = out_path + ".thd_api.o"
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+    res = subprocess.run([hipcc, *compile_flags(src), *san, "-c", "-o", obj, src],
+                         capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed on thd_api.hip (host sanitizer build)")
+    res = subprocess.run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                          "-Xarch_host", "-fsanitize=address", "-shared-libsan",
+                          "-o", out_path, obj, *others], capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc link failed (host sanitizer build)")
+    return out_path
+
+
 if __name__ == "__main__":
     build_library(verbose="--verbose" in sys.argv)
     print(LIB_PATH)
