@@ -34,10 +34,8 @@
  *   - Size limits (THD_ERR_SHAPE otherwise): total_q, total_kv < 2^31; a
  *     sequence's rows are addressed with 32-bit byte offsets, so
  *     max_seqlen_q * h_q * head_dim * 2 and max_seqlen_kv * h_kv * head_dim * 2
- *     must be below 2^31, and for the backward above head_dim 128 also
- *     max_seqlen_q * h_q * 256 * 4 (its fp32 dq accumulator) and
- *     total_q * h_q / 32.  max_seqlen_* must bound the true lengths: a longer
- *     sequence is clamped as above.
+ *     must be below 2^31.  max_seqlen_* must bound the true lengths: a
+ *     longer sequence is clamped as above.
  *   - No C++ exception crosses this interface.
  *
  * Sequence placement [I], [C]
@@ -161,17 +159,15 @@ int thd_attn_fwd_noalloc(const thd_varlen_args* args, const void* q, const void*
                          const void* v, void* o, float* lse, void* stream);
 
 /* Bytes of device workspace thd_attn_bwd needs for these arguments (per-row
- * fp32 statistics and the order of the work items, a few bytes per row; for
- * head_dim above 128 also an fp32 dq accumulator of total_q * h_q * 256
- * floats), 0 if the arguments are invalid.  The workspace needs no
- * initialisation. */
+ * fp32 statistics and the order of the work items, a few bytes per row),
+ * 0 if the arguments are invalid.  The workspace needs no initialisation. */
 size_t thd_attn_bwd_workspace_size(const thd_varlen_args* args);
 
 /* Backward: gradients of sum(o * dout) w.r.t. q, k and v [C] (Changes: Q/K/V
  * gradient parity).  o and lse are the forward's outputs for the same
  * inputs (D = rowsum(dout * o) is formed from o as given); dout is read only
- * at valid query rows.  For head_dim up to 128 nothing is accumulated with
- * atomics, so dq, dk and dv are deterministic.  dq, dk, dv have the shapes
+ * at valid query rows.  Nothing is accumulated with atomics, so dq, dk and
+ * dv are deterministic.  dq, dk, dv have the shapes
  * of q, k, v; every pad row is written as +0, key/value gradients of a GQA
  * group are summed over its query heads.  workspace must be a device buffer
  * of at least thd_attn_bwd_workspace_size(args) bytes, 256-byte aligned,
@@ -184,10 +180,8 @@ int thd_attn_bwd(const thd_varlen_args* args, const void* q, const void* k,
 /* thd_attn_bwd with timing marks: the same validation and launches, plus
  * hipEventRecord of events[0..3] (four hipEvent_t created by the caller) on
  * `stream` around its three launches -- before the pre pass, before the dq
- * pass, before the dk/dv pass and after it (head_dim up to 128); before the
- * pre pass, before the main gradient kernel, before the conversion pass and
- * after it (above 128) -- so that a caller can time each kernel on the stream
- * it runs on.  Errors: as thd_attn_bwd, THD_ERR_NULL if
+ * pass, before the dk/dv pass and after it -- so that a caller can time
+ * each kernel on the stream it runs on.  Errors: as thd_attn_bwd, THD_ERR_NULL if
  * an event is missing, THD_ERR_HIP if recording fails. */
 int thd_attn_bwd_timed(const thd_varlen_args* args, const void* q, const void* k,
                        const void* v, const void* o, const void* dout, const float* lse,

@@ -76,8 +76,7 @@ def test_fwd_rejects_invalid_arguments(kw, status):
 
 def test_sequence_size_limits():
     # 32-bit byte offsets per sequence: q / k / v rows of max_seqlen rows must
-    # stay below 2^31 bytes, and in the backward above head dim 128 the fp32
-    # dq accumulator rows (h_q * 256 * 4 bytes) too.
+    # stay below 2^31 bytes, in the forward and the backward alike.
     lib = _lib.load()
     fwd = lambda a: lib.thd_attn_fwd(ctypes.byref(a), P, P, P, P, P, P, 1 << 30, None)
     bwd = lambda a: lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, 1 << 30, None)
@@ -85,19 +84,17 @@ def test_sequence_size_limits():
     assert fwd(_args(**big_q)) == -2 and bwd(_args(**big_q)) == -2
     big_kv = dict(max_seqlen_kv=(1 << 31) // (2 * 64 * 2), total_kv=1 << 21)
     assert fwd(_args(**big_kv)) == -2 and bwd(_args(**big_kv)) == -2
-    # fits the 16-bit rows of d = 256 but not the backward's fp32 accumulator
-    acc_only = dict(max_seqlen_q=(1 << 31) // (4 * 256 * 4), total_q=1 << 20, head_dim=256)
-    assert bwd(_args(**acc_only)) == -2
-    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**acc_only))) == 0
-    # the forward passes the size checks and stops at the (empty) workspace,
-    # before anything could be launched with the placeholder pointers
-    assert lib.thd_attn_fwd(ctypes.byref(_args(**acc_only)), P, P, P, P, P, P, 0, None) == -4
-    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(**acc_only))) > 0
-    # up to head dim 128 the backward has no accumulator: the same rows at
-    # d = 128 pass its size checks and stop at the (empty) workspace
-    no_acc = dict(max_seqlen_q=(1 << 31) // (4 * 256 * 4), total_q=1 << 20, head_dim=128)
-    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**no_acc))) > 0
-    assert lib.thd_attn_bwd(ctypes.byref(_args(**no_acc)), P, P, P, P, P, P, P, P, P, P, 0,
+    wide_q = dict(max_seqlen_q=(1 << 31) // (4 * 256 * 2), total_q=1 << 20, head_dim=256)
+    assert fwd(_args(**wide_q)) == -2 and bwd(_args(**wide_q)) == -2
+    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**wide_q))) == 0
+    # one row fewer passes the size checks in both directions and stops at
+    # the (empty) workspace, before anything could be launched with the
+    # placeholder pointers
+    fits = dict(wide_q, max_seqlen_q=wide_q["max_seqlen_q"] - 1)
+    assert lib.thd_attn_fwd_workspace_size(ctypes.byref(_args(**fits))) > 0
+    assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(**fits))) > 0
+    assert lib.thd_attn_fwd(ctypes.byref(_args(**fits)), P, P, P, P, P, P, 0, None) == -4
+    assert lib.thd_attn_bwd(ctypes.byref(_args(**fits)), P, P, P, P, P, P, P, P, P, P, 0,
                             None) == -4
 
 
@@ -146,11 +143,11 @@ def test_workspace_size_and_check():
     a = _args()
     need = lib.thd_attn_bwd_workspace_size(ctypes.byref(a))
     # two fp32 row statistics [h_q, T_q], the dq pass's schedule of query
-    # tiles and the dk/dv pass's of key tiles (no fp32 dq accumulator at
-    # head dims up to 128); above 128, also the fp32 dq accumulator
+    # tiles and the dk/dv pass's of key tiles; nothing that grows with the
+    # head dim
     assert need >= 2 * 16 * 4 * 4 + 2 * (8 + 8 * (1 + 2)) * 4
-    wide = lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(head_dim=192)))
-    assert wide >= 16 * 4 * 256 * 4 + 2 * 16 * 4 * 4
+    for d in (8, 128, 192, 256):
+        assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(head_dim=d))) == need
     assert lib.thd_attn_bwd_workspace_size(ctypes.byref(_args(batch=-1))) == 0
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, P, need - 1, None) == -4
     assert lib.thd_attn_bwd(ctypes.byref(a), P, P, P, P, P, P, P, P, P, None, need, None) == -4

@@ -314,6 +314,21 @@ def test_forward_is_deterministic():
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
 
+@pytest.mark.parametrize("d", [64, 128, 192, 256])
+def test_backward_is_deterministic(d):
+    # no gradient is accumulated with atomics: two calls give the same bits,
+    # GQA group sums included
+    w = workloads.random_layout(127, batch=4, max_len=300, h_q=4, h_kv=2, d=d, dtype="bf16",
+                                causal="mixed")
+    print(f"case {w.name}: d={d}", flush=True)
+    q, k, v, do = (t.cuda() for t in workloads.make_tensors(w))
+    o, lse = gpu_fwd(w, q, k, v)
+    g1 = gpu_bwd(w, q, k, v, o, do, lse)
+    g2 = gpu_bwd(w, q, k, v, o, do, lse)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
 def test_empty_batch_writes_zeros():
     w = workloads.packed([], h_q=2, d=64)
     w.T_q = w.T_kv = 40

@@ -116,9 +116,12 @@ def build_host_asan_library(out_path):
     other sources' objects come from the last build_library run.  Device code
     is built as usual: the sanitizer flags are host-only."""
     objdir = os.path.join(PKG_DIR, "_build")
-    others = [o for o in sorted(glob.glob(os.path.join(objdir, "*.hip.o")))
-              if os.path.basename(o) != "thd_api.hip.o"]
-    if not others:
+    # the objects of the current sources only (a removed source's object may
+    # still sit in the build folder)
+    others = [os.path.join(objdir, os.path.basename(src) + ".o")
+              for src in sorted(glob.glob(os.path.join(CSRC, "*.hip")))
+              if os.path.basename(src) != "thd_api.hip"]
+    if not others or not all(os.path.exists(o) for o in others):
         raise RuntimeError("build_library() first: its objects are linked in")
     hipcc = hipcc_path()
     src = os.path.join(CSRC, "thd_api.hip")

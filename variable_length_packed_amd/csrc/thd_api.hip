@@ -21,22 +21,18 @@ bool aligned16(const void* ptr) { return ((uintptr_t)ptr & 15u) == 0; }
 
 // Kernels address a sequence's rows with 32-bit byte offsets from its first
 // row, so max_seqlen rows of every buffer they address per sequence must
-// stay below 2^31 bytes: q / o / dq rows (h_q * head_dim * 2 bytes), k / v
-// rows (h_kv * head_dim * 2) and, in the backward above head dim 128, the
-// fp32 dq accumulator rows (h_q * 256 * 4), whose pre and post passes also
-// take one workgroup per 32 (row, head) pairs.
-int check_sizes(const thd_varlen_args* a, bool backward) {
+// stay below 2^31 bytes: q / o / dq rows (h_q * head_dim * 2 bytes) and
+// k / v / dk / dv rows (h_kv * head_dim * 2).
+int check_sizes(const thd_varlen_args* a) {
   const int64_t lim = (int64_t)1 << 31;
-  const bool acc = backward && a->head_dim > 128;
-  const int64_t q_row = (int64_t)a->h_q * (acc ? 256 * 4 : a->head_dim * 2);
+  const int64_t q_row = (int64_t)a->h_q * a->head_dim * 2;
   const int64_t kv_row = (int64_t)a->h_kv * a->head_dim * 2;
   if ((int64_t)a->max_seqlen_q * q_row >= lim || (int64_t)a->max_seqlen_kv * kv_row >= lim)
     return THD_ERR_SHAPE;
-  if (acc && a->total_q * a->h_q / 32 >= lim) return THD_ERR_SHAPE;
   return THD_OK;
 }
 
-int to_problem(const thd_varlen_args* a, thd::Problem* p, bool backward) {
+int to_problem(const thd_varlen_args* a, thd::Problem* p) {
   if (!a) return THD_ERR_NULL;
   if (a->batch < 0 || a->max_seqlen_q < 0 || a->max_seqlen_kv < 0 || a->total_q < 0 ||
       a->total_kv < 0)
@@ -51,7 +47,7 @@ int to_problem(const thd_varlen_args* a, thd::Problem* p, bool backward) {
   const int64_t tiles_kv = (a->total_kv + 127) / 128 + a->batch;
   if (tiles_q * a->h_q >= ((int64_t)1 << 31) || tiles_kv * a->h_kv >= ((int64_t)1 << 31))
     return THD_ERR_SHAPE;
-  if (int st = check_sizes(a, backward)) return st;
+  if (int st = check_sizes(a)) return st;
   p->cu_q = a->cu_seqlens_q;
   p->cu_kv = a->cu_seqlens_kv;
   p->pad_q = a->cu_seqlens_q_padded;
@@ -82,7 +78,7 @@ int check_tensor(const void* ptr, int64_t rows) {
 // Host-visible checks of a forward call: the problem plus its tensors.
 int fwd_problem(const thd_varlen_args* args, const void* q, const void* k, const void* v,
                 const void* o, const float* lse, thd::Problem* p) {
-  int st = to_problem(args, p, false);
+  int st = to_problem(args, p);
   if (st != THD_OK) return st;
   const int64_t Tq = p->T_q, Tk = p->T_kv;
   if ((st = check_tensor(q, Tq)) || (st = check_tensor(o, Tq)) || (st = check_tensor(k, Tk)) ||
@@ -154,7 +150,7 @@ int thd_padding_mask(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqle
 
 size_t thd_attn_fwd_workspace_size(const thd_varlen_args* args) {
   thd::Problem p;
-  if (to_problem(args, &p, false) != THD_OK) return 0;
+  if (to_problem(args, &p) != THD_OK) return 0;
   return thd::fwd_workspace_bytes(p);
 }
 
@@ -187,7 +183,7 @@ int thd_attn_fwd_noalloc(const thd_varlen_args* args, const void* q, const void*
 
 size_t thd_attn_bwd_workspace_size(const thd_varlen_args* args) {
   thd::Problem p;
-  if (to_problem(args, &p, true) != THD_OK) return 0;
+  if (to_problem(args, &p) != THD_OK) return 0;
   return thd::bwd_workspace_bytes(p);
 }
 
@@ -196,7 +192,7 @@ static int attn_bwd_impl(const thd_varlen_args* args, const void* q, const void*
                          void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
                          void* stream, void* const* events) {
   thd::Problem p;
-  int st = to_problem(args, &p, true);
+  int st = to_problem(args, &p);
   if (st != THD_OK) return st;
   const int64_t Tq = p.T_q, Tk = p.T_kv;
   if ((st = check_tensor(q, Tq)) || (st = check_tensor(o, Tq)) ||

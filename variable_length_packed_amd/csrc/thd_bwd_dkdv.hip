@@ -1,4 +1,4 @@
-// dk/dv pass of the backward for head dims up to 128 (see thd_bwd_split.hip
+// dk/dv pass of the backward (see thd_bwd_split.hip
 // for the whole backward and its sources).
 //
 // One workgroup per (sequence, key tile of BK = 256 or 128 keys, kv head), in
@@ -17,7 +17,8 @@
 // the other buffer at the end, and one barrier per query tile publishes it.
 // BK = 128: one query tile (16K), K 32K, V 32K = 80K, two workgroups per CU;
 // the next tile is stored after a barrier that ends every wave's reads of the
-// current one, and a second barrier publishes it.  Tiles are row-major with
+// current one, and a second barrier publishes it.  DP = 256 takes BK = 128
+// only: 32K + 64K + 64K = 160K, one workgroup per CU.  Tiles are row-major with
 // swizzled 16-byte chunks (see swz).
 #include "thd_bwd_split.hpp"
 
@@ -35,7 +36,7 @@ namespace {
 constexpr int kDkdvBlocks = 1;
 
 template <class DT, int DP, int NB, int BK>
-__global__ __launch_bounds__(64 * BK / (32 * NB), 256 * NB / BK)
+__global__ __launch_bounds__(64 * BK / (32 * NB), DP > 128 ? 1 : 256 * NB / BK)
 void thd_bwd_dkdv_kernel(SplitParams p) {
   constexpr int BQ = kKvBQ, NQB = kKvQBufs<BK>;
   constexpr int NW = BK / (32 * NB);  // waves per workgroup
@@ -302,7 +303,7 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
         to[sl] = cat2(lds_read_tr(smem + TILE, t0), lds_read_tr(smem + TILE, t1));
         tq[sl] = cat2(lds_read_tr(smem, t0), lds_read_tr(smem, t1));
       };
-      constexpr int kVm = 8 / (2 * ND);
+      constexpr int kSteps = 2 * ND;  // statistics loads spread over the steps
       ld_t(0, 0);
 #pragma unroll
       for (int i = 0; i < 2 * ND; ++i) {
@@ -315,7 +316,8 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
           dk_acc[nb][dt] = DT::mfma(as_vec8<DT>(tq[i & 1]), db[nb][kb], dk_acc[nb][dt]);
         }
 #pragma unroll
-        for (int j = 0; j < kVm; ++j) load_stat(kVm * i + j);
+        for (int j = 0; j < 8; ++j)
+          if ((j * kSteps) / 8 == i) load_stat(j);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -367,12 +369,15 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
 template <class DT, int DP>
 hipError_t launch_dkdv(const SplitParams& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.n_ktiles * p.h_kv));
-  if (p.kv_bk == kKvBkLong)
-    hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkLong>), grid,
-                       dim3(64 * kKvBkLong / (32 * kDkdvBlocks)), 0, s, p);
-  else
-    hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkShort>), grid,
-                       dim3(64 * kKvBkShort / (32 * kDkdvBlocks)), 0, s, p);
+  if constexpr (DP <= 128) {
+    if (p.kv_bk == kKvBkLong) {
+      hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkLong>), grid,
+                         dim3(64 * kKvBkLong / (32 * kDkdvBlocks)), 0, s, p);
+      return hipGetLastError();
+    }
+  }
+  hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DT, DP, kDkdvBlocks, kKvBkShort>), grid,
+                     dim3(64 * kKvBkShort / (32 * kDkdvBlocks)), 0, s, p);
   return hipGetLastError();
 }
 
@@ -382,6 +387,8 @@ template hipError_t launch_dkdv<Bf16, 64>(const SplitParams&, hipStream_t);
 template hipError_t launch_dkdv<Fp16, 64>(const SplitParams&, hipStream_t);
 template hipError_t launch_dkdv<Bf16, 128>(const SplitParams&, hipStream_t);
 template hipError_t launch_dkdv<Fp16, 128>(const SplitParams&, hipStream_t);
+template hipError_t launch_dkdv<Bf16, 256>(const SplitParams&, hipStream_t);
+template hipError_t launch_dkdv<Fp16, 256>(const SplitParams&, hipStream_t);
 
 }  // namespace split
 }  // namespace thd

@@ -1,5 +1,5 @@
-// Backward attention over packed variable-length ("thd") tensors, head dims
-// up to 128: the gradients of TransformerEngine PR "Add per-sequence causal
+// Backward attention over packed variable-length ("thd") tensors (head dims
+// 8 to 256, padded to 32, 64, 128 or 256 in registers): the gradients of TransformerEngine PR "Add per-sequence causal
 // policy to packed THD attention" (Changes: Q/K/V gradient parity), in two
 // passes that each own their outputs, so that no gradient is accumulated with
 // atomics:
@@ -11,7 +11,8 @@
 //               the second pass;
 //   dk/dv pass: key-stationary: one workgroup per (sequence, key tile, kv
 //               head), 32 keys per wave (128-key tiles of 4 waves for short
-//               walks, 256-key tiles of 8 waves for long ones), walks the
+//               walks and for head dims above 128, 256-key tiles of 8 waves
+//               for long ones), walks the
 //               32-row query tiles of every query head of its GQA group,
 //               recomputes S and dP and accumulates dK^T and dV^T in
 //               registers (thd_bwd_dkdv.hip).
@@ -150,7 +151,7 @@ __global__ __launch_bounds__(256) void thd_bwd_split_pre_kernel(SplitParams p) {
 // of the same K tile.  K and V tiles go straight from memory into LDS, row
 // major with swizzled 16-byte chunks, as in the forward.
 template <class DT, int DP>
-__global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
+__global__ __launch_bounds__(256, DP > 128 ? 1 : 2) void thd_bwd_dq_kernel(SplitParams p) {
   constexpr int BM = kDqBM, BN = DqTile<DP>::BN;
   constexpr int NT = BN / 32;      // 32-key S^T tiles per LDS tile
   constexpr int NKB = BN / 16;     // 16-key blocks (K steps of dQ^T)
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(256, 2) void thd_bwd_dq_kernel(SplitParams p) {
                         f32x16 (&sn)[NT], f32x16 (&dpn)[NT]) {
     constexpr int NSEG = NT * NC;      // K steps of the next tile's products
     constexpr int EPS = 16 * NT / NSEG;  // dS elements per segment
-    static_assert(EPS * NSEG == 16 * NT && (EPS % 2 == 0), "whole element pairs per segment");
+    static_assert(EPS * NSEG == 16 * NT && EPS >= 1, "whole elements per segment");
     const uint32_t a_k = opaque(b_k + (uint32_t)(2 * bn * TILE));
     const uint32_t a_t = opaque(b_t + (uint32_t)(2 * bc * TILE));
     auto kv_addr = [&](int g) {
@@ -472,7 +473,7 @@ int64_t split_qtiles(const Problem& p) { return (p.T_q + kDqBM - 1) / kDqBM + p.
 // Keys per dk/dv workgroup, from host scalars only: a key tile walks at most
 // max_seqlen_q rows of each of the group's query heads.
 int split_kv_bk(const Problem& p) {
-  return (int64_t)p.max_q * (p.h_q / p.h_kv) <= kKvShortWalkRows ? kKvBkShort : kKvBkLong;
+  return p.d > 128 || (int64_t)p.max_q * (p.h_q / p.h_kv) <= kKvShortWalkRows ? kKvBkShort : kKvBkLong;
 }
 int64_t split_ktiles(const Problem& p) {
   const int bk = split_kv_bk(p);
@@ -484,17 +485,16 @@ int64_t split_ktiles(const Problem& p) {
 // -D and -LSE/scale ([h_q][T_q] fp32 each), then the dq pass's schedule
 // (sched_bytes of the query-tile bound) and the dk/dv pass's (of the
 // key-tile bound).
-size_t split_bwd_workspace_bytes(const Problem& p) {
+size_t bwd_workspace_bytes(const Problem& p) {
   const size_t stats = align256_s((size_t)p.T_q * p.h_q * 2 * sizeof(float));
   const size_t qs = align256_s(sched_bytes(split_qtiles(p)));
   const size_t ks = align256_s(sched_bytes(split_ktiles(p)));
   return stats + qs + ks;
 }
 
-hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, const void* v,
-                            const void* o, const void* dout, const float* lse, void* dq,
-                            void* dk, void* dv, void* workspace, hipStream_t s,
-                            hipEvent_t const* ev) {
+hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
+                      const void* o, const void* dout, const float* lse, void* dq, void* dk,
+                      void* dv, void* workspace, hipStream_t s, hipEvent_t const* ev) {
   SplitParams sp;
   sp.q = (const uint16_t*)q;
   sp.k = (const uint16_t*)k;
@@ -539,7 +539,9 @@ hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, cons
     return p.bf16 ? launch_split_t<Bf16, 32>(sp, n_pre, s, ev) : launch_split_t<Fp16, 32>(sp, n_pre, s, ev);
   if (p.d <= 64)
     return p.bf16 ? launch_split_t<Bf16, 64>(sp, n_pre, s, ev) : launch_split_t<Fp16, 64>(sp, n_pre, s, ev);
-  return p.bf16 ? launch_split_t<Bf16, 128>(sp, n_pre, s, ev) : launch_split_t<Fp16, 128>(sp, n_pre, s, ev);
+  if (p.d <= 128)
+    return p.bf16 ? launch_split_t<Bf16, 128>(sp, n_pre, s, ev) : launch_split_t<Fp16, 128>(sp, n_pre, s, ev);
+  return p.bf16 ? launch_split_t<Bf16, 256>(sp, n_pre, s, ev) : launch_split_t<Fp16, 256>(sp, n_pre, s, ev);
 }
 
 }  // namespace thd

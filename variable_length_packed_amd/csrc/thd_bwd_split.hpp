@@ -1,5 +1,5 @@
-// Internal interface between the two sources of the backward for head dims
-// up to 128 (thd_bwd_split.hip: pre pass, dq pass and launch;
+// Internal interface between the two sources of the backward
+// (thd_bwd_split.hip: pre pass, dq pass and launch;
 // thd_bwd_dkdv.hip: the dk/dv pass, built with its own compiler options).
 #pragma once
 
@@ -10,7 +10,8 @@ namespace split {
 
 constexpr int kDqBM = 128;   // query rows per dq workgroup (4 waves of 32 rows)
 // The dk/dv pass's two shapes, chosen on the host from the length of its
-// walks (max_seqlen_q times the GQA group):
+// walks (max_seqlen_q times the GQA group); above head dim 128 always the
+// short one (the long one's LDS would not fit):
 //   long walks : 256 keys (8 waves), Q and dO of two query tiles in LDS
 //                (160 KB, one workgroup per CU, one barrier per query tile);
 //   short walks: 128 keys (4 waves), one query tile in LDS (80 KB, two

@@ -39,19 +39,10 @@ hipError_t launch_decode(const Problem& p, const void* q, const void* k, const v
 hipError_t launch_fwd(const Problem& p, const void* q, const void* k, const void* v, void* o,
                       float* lse, void* workspace, hipStream_t s);
 
-size_t bwd_workspace_bytes(const Problem& p);
-
-// The backward for head dims up to 128 as a dq pass and a dk/dv pass (see
-// thd_bwd_split.hip); `events` as launch_bwd's (before the pre pass, the dq
-// pass, the dk/dv pass, and after it).
-size_t split_bwd_workspace_bytes(const Problem& p);
-hipError_t launch_bwd_split(const Problem& p, const void* q, const void* k, const void* v,
-                            const void* o, const void* dout, const float* lse, void* dq,
-                            void* dk, void* dv, void* workspace, hipStream_t s,
-                            hipEvent_t const* events);
-
+// The backward as a dq pass and a dk/dv pass (thd_bwd_split.hip, thd_bwd_dkdv.hip).
 // `events` is null or four events recorded on `s` before the pre pass, before
-// the main kernel, before the post pass and after it.
+// the dq pass, before the dk/dv pass and after it.
+size_t bwd_workspace_bytes(const Problem& p);
 hipError_t launch_bwd(const Problem& p, const void* q, const void* k, const void* v,
                       const void* o, const void* dout, const float* lse, void* dq, void* dk,
                       void* dv, void* workspace, hipStream_t s,
