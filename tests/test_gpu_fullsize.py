@@ -5,7 +5,8 @@ alone); dk/dv of the shortest sequence, the one with the most query rows and
 the one with the most keys -- whole when the oracle is cheap, else the first,
 a middle and the last 256-key tile over every query head of one kv head (the
 oracle takes such a key range by query-row blocks); and every pad row
-bit-exact +0."""
+bit-exact +0.  The same checks run on config 2's lengths at head dims 192 and
+256 (fewer heads), so that the 256-wide kernels walk full-length sequences."""
 import numpy as np
 import pytest
 import torch
@@ -27,8 +28,8 @@ WHOLE_PAIRS = 1 << 23
 TILE = 256
 
 
-def check_config(name, n_row_seqs=3):
-    w = workloads.config(name)
+def check_config(name, n_row_seqs=3, w=None):
+    w = workloads.config(name) if w is None else w
     print(f"config {name}: B={w.batch} Tq={w.T_q} Tkv={w.T_kv} h={w.h_q}/{w.h_kv}", flush=True)
     q, k, v, do = workloads.make_tensors(w, device="cuda")
     meta = dev_meta(w)
@@ -41,7 +42,7 @@ def check_config(name, n_row_seqs=3):
         assert torch.isfinite(t.float()).all(), nm
     sq, sk = w.starts_q(), w.starts_kv()
     group = w.h_q // w.h_kv
-    rng = np.random.default_rng(1000 + int(name))
+    rng = np.random.default_rng(1000 + int(str(name).split("-")[0]))
     order = np.argsort(w.lens_q)
     row_seqs = sorted({int(order[-1]), int(order[0]), int(order[len(order) // 2])})[:n_row_seqs]
     # --- sampled query rows: out, lse, dq --------------------------------
@@ -112,3 +113,19 @@ def check_config(name, n_row_seqs=3):
 @pytest.mark.parametrize("name", ["2", "3", "5", "4", "6", "7"])
 def test_full_size_config(name):
     check_config(name)
+
+
+def wide_head_config(d, dtype):
+    """Config 2's lengths (16 causal sequences of 64 to 2,048 tokens) at a
+    head dim above 128, 4 query heads over 2 kv heads."""
+    rng = np.random.default_rng(2)
+    lens = rng.integers(64, 2048, size=16, endpoint=True)
+    return workloads.packed(lens, causal=np.ones(16, np.uint8), h_q=4, h_kv=2, d=d,
+                            dtype=dtype, seed=2, name=f"2-d{d}")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("d,dtype", [(192, "bf16"), (256, "fp16"), (256, "bf16")])
+def test_full_length_wide_heads(d, dtype):
+    # the backward's 256-wide passes walk up to 2,034 rows per key tile here
+    check_config(f"2-d{d}", w=wide_head_config(d, dtype))
