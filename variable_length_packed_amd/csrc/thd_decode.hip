@@ -14,10 +14,19 @@
 //   M = max_c m_c,  L = sum_c l_c 2^(m_c - M),  O = sum_c O_c 2^(m_c - M) / L,
 //   LSE = (M + log2 L) ln 2   (m in log2 units of the scaled scores).
 //
-// Per 32-key step a wave computes S^T = K Q^T (keys x query rows; K is read
-// from HBM straight into the A operand), applies the mask and the online
-// softmax, stages the 32 V rows in its own LDS tile and adds V^T P^T, whose
-// A operand comes from transpose reads of that tile.
+// Per 32-key step a wave loads the step's 32 K and V rows whole (each load
+// instruction covers four 256-byte rows of its kv head), stages K in its own
+// LDS tile and reads the A operand of S^T = K Q^T (keys x query rows) from
+// it, applies the mask and the online softmax, stages V in a second tile and
+// adds V^T P^T, whose A operand comes from transpose reads of that tile.
+// Workgroups run kv heads minor, so the heads of one (sequence, chunk) read
+// the same packed K/V rows at the same time.  Chunks past a sequence's last
+// visible key write nothing; the merge reads only the chunks below it.
+// (On 64 decode sequences against 256-16,384 keys, GQA 32/8, d = 128: K loaded
+// straight into the A operand -- 32 B of each of 32 rows per instruction --
+// 0.603 ms; K staged whole 0.556; both with heads minor 0.525; and without
+// the empty chunks' writes 0.505.  A copy of the pass that only loads its
+// K/V takes 0.492 ms.)
 #include <limits.h>
 
 #include "thd_common.hpp"
@@ -36,6 +45,7 @@ struct DecParams {
   const uint16_t* v;
   uint16_t* o;
   float* lse;
+  // per (row, chunk); chunks past a sequence's last visible key stay unwritten
   float* part_o;   // [rows * n_split][DP]: unnormalised partial outputs
   float* part_ml;  // [rows * n_split][2]: max (log2 units) and row sum
   const int32_t* cu_q;
@@ -52,7 +62,7 @@ struct DecParams {
 };
 
 // ---------------------------------------------------------------------------
-// split: one wave per (sequence, kv head, key chunk)
+// split: one wave per (sequence, key chunk, kv head), kv heads minor
 // ---------------------------------------------------------------------------
 template <class DT, int DP>
 __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
@@ -60,11 +70,12 @@ __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
   constexpr int ND = DP / 32;
   constexpr int KCH = DP / 8;
   __shared__ __attribute__((aligned(16))) unsigned char Vs[kDecStep * DP * 2];
+  __shared__ __attribute__((aligned(16))) unsigned char Ks[kDecStep * DP * 2];
 
-  const int split = blockIdx.x % p.n_split;
-  const int rest = blockIdx.x / p.n_split;
-  const int hk = rest % p.h_kv;
-  const int b = rest / p.h_kv;
+  const int hk = blockIdx.x % p.h_kv;
+  const int rest = blockIdx.x / p.h_kv;
+  const int split = rest % p.n_split;
+  const int b = rest / p.n_split;
   const int l = threadIdx.x;
   const int r = l & 31;
   const int h = l >> 5;
@@ -96,6 +107,7 @@ __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
   const int k_lo = split * p.ck;
   int k_hi = min(k_lo + p.ck, lk);
   if (causal && lq + off < k_hi) k_hi = lq + off;
+  if (k_lo >= k_hi) return;  // no key of this chunk is visible: nothing to merge
   const int lim_r = min(lim, k_hi);
 
   // Q as the B operand of S^T = K Q^T: lane (r, h) holds Q[row r][16c + 8h ..].
@@ -122,24 +134,34 @@ __global__ __launch_bounds__(64) void thd_decode_split_kernel(DecParams p) {
   float l_run = 0.f;                // this lane's share of the row sum
   const float c2 = p.c2;
 
+  constexpr int NV = kDecStep * KCH / 64;
   for (int j0 = k_lo; j0 < k_hi; j0 += kDecStep) {
-    // K rows j0 + r as the A operand; rows past lk read as zeros.
-    u32x4 ka[NC];
+    // K and V rows j0 .. j0+31, KCH 16-byte chunks each: lane l takes chunks
+    // l + 64u; rows past lk read as zeros
+    u32x4 kr[NV], vr[NV];
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int dd = 16 * c + 8 * h;
-      ka[c] = buf_load16(k_rs, dd < p.d ? (uint32_t)(j0 + r) * kvrow_bytes + 2u * dd : kOobOffset, 0);
-    }
-    // V rows j0 .. j0+31 (KCH chunks each) for the LDS tile.
-    u32x4 vr[kDecStep * KCH / 64];
-#pragma unroll
-    for (int u = 0; u < kDecStep * KCH / 64; ++u) {
+    for (int u = 0; u < NV; ++u) {
       const int cid = l + 64 * u;
       const int row = cid / KCH;
       const int x = cid - row * KCH;
-      vr[u] = buf_load16(v_rs, 8 * x < p.d ? (uint32_t)(j0 + row) * kvrow_bytes + 16u * x : kOobOffset, 0);
+      const uint32_t o = 8 * x < p.d ? (uint32_t)(j0 + row) * kvrow_bytes + 16u * x : kOobOffset;
+      kr[u] = buf_load16(k_rs, o, 0);
+      vr[u] = buf_load16(v_rs, o, 0);
     }
-
+    // K tile -> LDS, then the A operand of S^T = K Q^T: lane (r, h) reads
+    // K[row r][16c + 8h ..]
+    __syncthreads();  // the previous step's K reads are done
+#pragma unroll
+    for (int u = 0; u < NV; ++u) {
+      const int cid = l + 64 * u;
+      const int row = cid / KCH;
+      const int x = cid - row * KCH;
+      *(u32x4*)(Ks + swz<DP>(row, 8 * x)) = kr[u];
+    }
+    __syncthreads();  // K tile complete
+    u32x4 ka[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) ka[c] = *(const u32x4*)(Ks + swz<DP>(r, 16 * c + 8 * h));
     f32x16 s = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) s = DT::mfma(as_vec8<DT>(ka[c]), qreg[c], s);
@@ -239,24 +261,44 @@ __global__ __launch_bounds__(256) void thd_decode_merge_kernel(DecParams p) {
   const int64_t sq = seq_start(p.cu_q, p.pad_q, b);
   const int lq = clamp_rows(sq, seq_len_clamped(p.cu_q, b, p.T_q), p.T_q, qrow_bytes);
   if (qi >= lq) return;  // past the sequence: a pad row, or a row of the next one
+  // the chunks the split pass wrote: those below the sequence's last visible key
+  const uint32_t kvrow_bytes = (uint32_t)p.h_kv * p.d * 2;
+  const int64_t sk = seq_start(p.cu_kv, p.pad_kv, b);
+  const int lk = clamp_rows(sk, seq_len_clamped(p.cu_kv, b, p.T_kv), p.T_kv, kvrow_bytes);
+  const int mtype = mask_type_of(p.mask_type, b);
+  int k_end = lk;
+  if (mask_is_causal(mtype)) k_end = min(k_end, lq + causal_offset(mtype, lq, lk));
+  const int n_valid = k_end > 0 ? min(p.n_split, (k_end + p.ck - 1) / p.ck) : 0;
 
+  // Lane l takes chunks l, l + 64, ...: the maximum, then the weighted row
+  // sum; the chunks' outputs are then added with every lane on its columns.
+  // No step waits on the previous chunk's loads (a loop that branched on each
+  // chunk's maximum before loading its output took 33 against 17 us on 64 decode
+  // sequences against 256-16,384 keys).
   const int64_t base = row_id * p.n_split;
   float M = -__builtin_inff();
-  for (int s = l; s < p.n_split; s += 64) M = fmaxf(M, p.part_ml[2 * (base + s)]);
+  for (int s = l; s < n_valid; s += 64) M = fmaxf(M, p.part_ml[2 * (base + s)]);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  float L = 0.f;
+  if (M != -__builtin_inff())
+    for (int s = l; s < n_valid; s += 64) {
+      const float ms = p.part_ml[2 * (base + s)];
+      if (ms != -__builtin_inff()) L += p.part_ml[2 * (base + s) + 1] * __builtin_amdgcn_exp2f(ms - M);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) L += __shfl_xor(L, o, 64);
 
   constexpr int PER = DP / 64 > 0 ? DP / 64 : 1;  // output columns per lane
   float accv[PER];
 #pragma unroll
   for (int e = 0; e < PER; ++e) accv[e] = 0.f;
-  float L = 0.f;
   if (M != -__builtin_inff()) {
-    for (int s = 0; s < p.n_split; ++s) {
+    // a chunk with no visible key for this row holds zeros and weighs 0
+#pragma unroll 4
+    for (int s = 0; s < n_valid; ++s) {
       const float ms = p.part_ml[2 * (base + s)];
-      if (ms == -__builtin_inff()) continue;  // a chunk with no visible key
-      const float wgt = __builtin_amdgcn_exp2f(ms - M);
-      L += p.part_ml[2 * (base + s) + 1] * wgt;
+      const float wgt = ms == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(ms - M);
       const float* po = p.part_o + (base + s) * DP;
 #pragma unroll
       for (int e = 0; e < PER; ++e) {
