@@ -339,28 +339,47 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
                                  kv_bytes);
   const rsrc_t dv_rs = make_rsrc(p.dv + (sk + k0) * (int64_t)p.h_kv * p.d + (int64_t)hk * p.d,
                                  kv_bytes);
+  // Each wave stages its key blocks' dK and dV (bf16, row-major, swizzled) in
+  // its own part of the K/V tiles, free once the walk is over, then stores
+  // whole rows: each store covers 64 / KCH full rows.  (Stored straight from
+  // the accumulators, 8 bytes per lane and 32 rows per store, the pass took
+  // 0.247 against 0.229 ms on 16 causal sequences of 64-2,048 tokens, h 16,
+  // d 128, and 0.96 against 0.78 ms on 32 cross-attention pairs.)
+  static_assert(2 * NB * 32 * DP * 2 * NW <= 2 * BK * DP * 2, "staging fits the K/V tiles");
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const uint32_t krow = (uint32_t)(32 * (NB * w + nb) + r) * kvrow_bytes;
+    unsigned char* st_k = smem + OFF_K + (size_t)(2 * (NB * w + nb)) * 32 * DP * 2;
+    unsigned char* st_v = st_k + 32 * DP * 2;
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
       for (int gq = 0; gq < 4; ++gq) {
         const int dd = 32 * dt + 8 * gq + 4 * h;
-        if (dd < p.d) {
-          u32x2 ok, ov;
-          ok[0] = (uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 0] * p.scale) |
-                  ((uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 1] * p.scale) << 16);
-          ok[1] = (uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 2] * p.scale) |
-                  ((uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 3] * p.scale) << 16);
-          ov[0] = (uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 0]) |
-                  ((uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 1]) << 16);
-          ov[1] = (uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 2]) |
-                  ((uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 3]) << 16);
-          buf_store8(ok, dk_rs, krow + 2u * dd, 0);
-          buf_store8(ov, dv_rs, krow + 2u * dd, 0);
-        }
+        u32x2 ok, ov;
+        ok[0] = (uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 0] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 1] * p.scale) << 16);
+        ok[1] = (uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 2] * p.scale) |
+                ((uint32_t)DT::bits(dk_acc[nb][dt][4 * gq + 3] * p.scale) << 16);
+        ov[0] = (uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 0]) |
+                ((uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 1]) << 16);
+        ov[1] = (uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 2]) |
+                ((uint32_t)DT::bits(dv_acc[nb][dt][4 * gq + 3]) << 16);
+        *(u32x2*)(st_k + swz<DP>(r, dd)) = ok;
+        *(u32x2*)(st_v + swz<DP>(r, dd)) = ov;
       }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 32 * KCH / 64; ++j) {
+      const int c = l + 64 * j;
+      const int row = c / KCH, x = c - row * KCH;
+      const u32x4 vk = *(const u32x4*)(st_k + swz<DP>(row, 8 * x));
+      const u32x4 vv = *(const u32x4*)(st_v + swz<DP>(row, 8 * x));
+      const uint32_t o = 8 * x < p.d ? (uint32_t)(32 * (NB * w + nb) + row) * kvrow_bytes + 16u * x
+                                     : kOobOffset;
+      buf_store16(vk, dk_rs, o, 0);
+      buf_store16(vv, dv_rs, o, 0);
+    }
   }
 }
 

@@ -424,21 +424,32 @@ __global__ __launch_bounds__(256, DP > 128 ? 1 : 2) void thd_bwd_dq_kernel(Split
   }
 
   // dq = scale dQ; rows past lq are dropped by the resource bound.
-  const uint32_t orow = (uint32_t)my_q * qrow_bytes;
+  // Each wave stages its 32 rows (bf16, row-major, swizzled) in its own part
+  // of the K/V tiles, which every wave is done with after the walk's last
+  // barrier, then stores whole rows: each store covers 64 / KCH full rows.
+  static_assert(4 * 32 * DP * 2 <= 2 * kDqBufs * TILE, "staging fits the K/V tiles");
+  unsigned char* st = smem + (size_t)w * 32 * DP * 2;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = 32 * dt + 8 * g + 4 * h;
-      if (dd < p.d) {
-        u32x2 out;
-        out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * p.scale) |
-                 ((uint32_t)DT::bits(acc[dt][4 * g + 1] * p.scale) << 16);
-        out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * p.scale) |
-                 ((uint32_t)DT::bits(acc[dt][4 * g + 3] * p.scale) << 16);
-        buf_store8(out, dq_rs, orow + 2u * dd, 0);
-      }
+      u32x2 out;
+      out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * p.scale) |
+               ((uint32_t)DT::bits(acc[dt][4 * g + 1] * p.scale) << 16);
+      out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * p.scale) |
+               ((uint32_t)DT::bits(acc[dt][4 * g + 3] * p.scale) << 16);
+      *(u32x2*)(st + swz<DP>(r, dd)) = out;
     }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 32 * KCH / 64; ++j) {
+    const int c = l + 64 * j;
+    const int row = c / KCH, x = c - row * KCH;
+    const u32x4 v = *(const u32x4*)(st + swz<DP>(row, 8 * x));
+    // rows past lq are dropped by the resource bound
+    buf_store16(v, dq_rs, 8 * x < p.d ? (uint32_t)(qw0 + row) * qrow_bytes + 16u * x : kOobOffset, 0);
+  }
 }
 
 template <class DT, int DP>

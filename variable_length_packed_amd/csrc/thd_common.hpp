@@ -184,16 +184,9 @@ __device__ __forceinline__ void buf_load_lds16(u32x4 rs, uint32_t lds_wave, uint
 }
 #pragma clang diagnostic pop
 
-__device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), r, (int)voff, (int)soff, 0);
-}
-
-__device__ __forceinline__ void buf_store4(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, (int)voff, (int)soff, 0);
-}
-
-__device__ __forceinline__ void buf_atomic_add(float v, rsrc_t r, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(v, r, (int)voff, (int)soff, 0);
+// 16 bytes per lane (the kernels' outputs are stored as whole rows)
+__device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
 }
 
 // ---------------------------------------------------------------------------

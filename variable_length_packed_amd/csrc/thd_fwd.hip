@@ -374,21 +374,32 @@ __global__ __launch_bounds__(256, FwdTile<DP>::WG_PER_CU) void thd_fwd_kernel(Fw
   // by the resource bound.
   const float lt = wave_sum_halves(l_run);
   const float inv = lt > 0.f ? 1.f / lt : 0.f;
-  const uint32_t orow = (uint32_t)my_q * qrow_bytes;
+  // Each wave stages its 32 rows (bf16, row-major, swizzled) in its own part
+  // of the K/V tiles, which every wave is done with after the walk's last
+  // barrier, then stores whole rows: each store covers 64 / KCH full rows.
+  static_assert(4 * 32 * DP * 2 <= 2 * NS * TILE, "staging fits the K/V tiles");
+  unsigned char* st = smem + (size_t)w * 32 * DP * 2;
 #pragma unroll
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       const int dd = 32 * dt + 8 * g + 4 * h;
-      if (dd < p.d) {
-        u32x2 out;
-        out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * inv) |
-                 ((uint32_t)DT::bits(acc[dt][4 * g + 1] * inv) << 16);
-        out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * inv) |
-                 ((uint32_t)DT::bits(acc[dt][4 * g + 3] * inv) << 16);
-        buf_store8(out, o_rs, orow + 2u * dd, 0);
-      }
+      u32x2 out;
+      out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * inv) |
+               ((uint32_t)DT::bits(acc[dt][4 * g + 1] * inv) << 16);
+      out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * inv) |
+               ((uint32_t)DT::bits(acc[dt][4 * g + 3] * inv) << 16);
+      *(u32x2*)(st + swz<DP>(r, dd)) = out;
     }
+  asm volatile("" ::: "memory");
+#pragma unroll
+  for (int j = 0; j < 32 * KCH / 64; ++j) {
+    const int c = l + 64 * j;
+    const int row = c / KCH, x = c - row * KCH;
+    const u32x4 v = *(const u32x4*)(st + swz<DP>(row, 8 * x));
+    // rows past lq are dropped by the resource bound
+    buf_store16(v, o_rs, 8 * x < p.d ? (uint32_t)(qw0 + row) * qrow_bytes + 16u * x : kOobOffset, 0);
+  }
   if (h == 0 && my_q < lq)
     p.lse[(int64_t)hq * p.T_q + sq + my_q] =
         lt > 0.f ? m_run * p.scale + __logf(lt) : -__builtin_inff();
