@@ -162,8 +162,10 @@ __global__ __launch_bounds__(256, DP > 128 ? 1 : 2) void thd_bwd_dq_kernel(Split
   constexpr int BPW = TILE / 1024 / 4;
   static_assert(BPW >= 1 && BPW * 4096 == TILE, "tile splits into 1 KB blocks over 4 waves");
   static_assert(2 * BPW < 16, "loads of one tile fit the vmcnt field");
-  // buffer j: K tile at 2j TILE, V tile at (2j + 1) TILE
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDqBufs * TILE];
+  // buffer j: K tile at 2j TILE, V tile at (2j + 1) TILE; then (DP = 128) a
+  // [32][DP] tile per wave through which its Q and dO rows pass
+  constexpr int ROWS = DP == 128 ? 32 * DP * 2 : 0;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[2 * kDqBufs * TILE + 4 * ROWS];
 
   const int bid = blockIdx.x;
   const int rk = bid / p.h_q;
@@ -242,22 +244,77 @@ __global__ __launch_bounds__(256, DP > 128 ? 1 : 2) void thd_bwd_dq_kernel(Split
   // d 16c + 8h .. +7; D = rowsum(dO * O) over the same chunks of O, the two
   // halves of a row meeting across lanes r and r + 32.
   typename DT::vec8 qreg[NC], greg[NC];
-  float dpart = 0.f;
+  float Drow;
+  if constexpr (DP == 128) {
+    // Whole rows: load j of the wave covers rows RPI j .. RPI j + RPI - 1,
+    // lane l the 16-byte chunk l % KCH of row RPI j + l / KCH.  (Loaded
+    // straight into the operand layout, 32 bytes of each of 32 rows per load,
+    // the pass took 0.178 against 0.175 ms on 16 causal sequences of
+    // 64-2,048 tokens, h 16, d 128, and 0.543 against 0.520 ms on 64 padded
+    // sequences of up to 1,024 tokens, h 32.)
+    constexpr int RPI = 64 / KCH, NJ = 32 / RPI;
+    unsigned char* st = smem + 2 * kDqBufs * TILE + w * ROWS;
+    u32x4 qv[NJ], gv[NJ], ov[NJ];
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int dd = 16 * c + 8 * h;
-    const uint32_t o = dd < p.d ? (uint32_t)my_q * qrow_bytes + 2u * dd : kOobOffset;
-    qreg[c] = as_vec8<DT>(buf_load16(q_rs, o, 0));
-    const u32x4 gv = buf_load16(g_rs, o, 0);
-    const u32x4 ov = buf_load16(o_rs, o, 0);
-    greg[c] = as_vec8<DT>(gv);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dpart += DT::to_f32((uint16_t)(gv[j] & 0xffffu)) * DT::to_f32((uint16_t)(ov[j] & 0xffffu));
-      dpart += DT::to_f32((uint16_t)(gv[j] >> 16)) * DT::to_f32((uint16_t)(ov[j] >> 16));
+    for (int j = 0; j < NJ; ++j) {
+      const int row = RPI * j + l / KCH, x = l % KCH;
+      const uint32_t o = 8 * x < p.d ? (uint32_t)(qw0 + row) * qrow_bytes + 16u * x : kOobOffset;
+      qv[j] = buf_load16(q_rs, o, 0);
+      gv[j] = buf_load16(g_rs, o, 0);
+      ov[j] = buf_load16(o_rs, o, 0);
     }
+    // Q: rows into the tile, then lane (r, h) reads Q[r][16c + 8h ..]
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *(u32x4*)(st + swz<DP>(RPI * j + l / KCH, 8 * (l % KCH))) = qv[j];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < NC; ++c) qreg[c] = as_vec8<DT>(*(const u32x4*)(st + swz<DP>(r, 16 * c + 8 * h)));
+    asm volatile("" ::: "memory");
+    // D = rowsum(dO * O): a row's KCH lanes sum their chunks; its sum goes to
+    // word row of the tile (whose Q reads are done), where lanes r read it
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      float dp_ = 0.f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dp_ += DT::to_f32((uint16_t)(gv[j][e] & 0xffffu)) * DT::to_f32((uint16_t)(ov[j][e] & 0xffffu));
+        dp_ += DT::to_f32((uint16_t)(gv[j][e] >> 16)) * DT::to_f32((uint16_t)(ov[j][e] >> 16));
+      }
+      dp_ = group_sum<KCH>(dp_);
+      if (l % KCH == 0) ((float*)st)[RPI * j + l / KCH] = dp_;
+    }
+    asm volatile("" ::: "memory");
+    Drow = ((const float*)st)[r];
+    asm volatile("" ::: "memory");
+    // dO: rows into the tile, then the operand reads as for Q
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      *(u32x4*)(st + swz<DP>(RPI * j + l / KCH, 8 * (l % KCH))) = gv[j];
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int c = 0; c < NC; ++c) greg[c] = as_vec8<DT>(*(const u32x4*)(st + swz<DP>(r, 16 * c + 8 * h)));
+  } else {
+    // Q and dO as the B operands of S^T and dP^T: lane holds row my_q,
+    // d 16c + 8h .. +7; D = rowsum(dO * O) over the same chunks of O, the two
+    // halves of a row meeting across lanes r and r + 32.
+    float dpart = 0.f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int dd = 16 * c + 8 * h;
+      const uint32_t o = dd < p.d ? (uint32_t)my_q * qrow_bytes + 2u * dd : kOobOffset;
+      qreg[c] = as_vec8<DT>(buf_load16(q_rs, o, 0));
+      const u32x4 gv = buf_load16(g_rs, o, 0);
+      const u32x4 ov = buf_load16(o_rs, o, 0);
+      greg[c] = as_vec8<DT>(gv);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dpart += DT::to_f32((uint16_t)(gv[j] & 0xffffu)) * DT::to_f32((uint16_t)(ov[j] & 0xffffu));
+        dpart += DT::to_f32((uint16_t)(gv[j] >> 16)) * DT::to_f32((uint16_t)(ov[j] >> 16));
+      }
+    }
+    Drow = wave_sum_halves(dpart);
   }
-  const float Drow = wave_sum_halves(dpart);
   float lse_row = 0.f;
   if (my_q < lq) lse_row = p.lse[(int64_t)hq * p.T_q + sq + my_q];
   // statistics of this row for the dk/dv pass
@@ -424,31 +481,51 @@ __global__ __launch_bounds__(256, DP > 128 ? 1 : 2) void thd_bwd_dq_kernel(Split
   }
 
   // dq = scale dQ; rows past lq are dropped by the resource bound.
-  // Each wave stages its 32 rows (bf16, row-major, swizzled) in its own part
-  // of the K/V tiles, which every wave is done with after the walk's last
-  // barrier, then stores whole rows: each store covers 64 / KCH full rows.
-  static_assert(4 * 32 * DP * 2 <= 2 * kDqBufs * TILE, "staging fits the K/V tiles");
-  unsigned char* st = smem + (size_t)w * 32 * DP * 2;
+  if constexpr (DP != 64) {
+    // Each wave stages its 32 rows (bf16, row-major, swizzled) in its own part
+    // of the K/V tiles, which every wave is done with after the walk's last
+    // barrier, then stores whole rows: each store covers 64 / KCH full rows.
+    static_assert(4 * 32 * DP * 2 <= 2 * kDqBufs * TILE, "staging fits the K/V tiles");
+    unsigned char* st = smem + (size_t)w * 32 * DP * 2;
 #pragma unroll
-  for (int dt = 0; dt < ND; ++dt)
+    for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int dd = 32 * dt + 8 * g + 4 * h;
-      u32x2 out;
-      out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * p.scale) |
-               ((uint32_t)DT::bits(acc[dt][4 * g + 1] * p.scale) << 16);
-      out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * p.scale) |
-               ((uint32_t)DT::bits(acc[dt][4 * g + 3] * p.scale) << 16);
-      *(u32x2*)(st + swz<DP>(r, dd)) = out;
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * dt + 8 * g + 4 * h;
+        u32x2 out;
+        out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * p.scale) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 1] * p.scale) << 16);
+        out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * p.scale) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 3] * p.scale) << 16);
+        *(u32x2*)(st + swz<DP>(r, dd)) = out;
+      }
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int j = 0; j < 32 * KCH / 64; ++j) {
+      const int c = l + 64 * j;
+      const int row = c / KCH, x = c - row * KCH;
+      const u32x4 v = *(const u32x4*)(st + swz<DP>(row, 8 * x));
+      // rows past lq are dropped by the resource bound
+      buf_store16(v, dq_rs, 8 * x < p.d ? (uint32_t)(qw0 + row) * qrow_bytes + 16u * x : kOobOffset, 0);
     }
-  asm volatile("" ::: "memory");
+  } else {
+    // At DP = 64 the staging's registers would cost the third wave per SIMD
+    // (171 against 168 VGPRs; the pass took 0.102 against 0.097 ms at h 16 on
+    // the same layout), so dq leaves straight from the accumulators, 8 bytes
+    // per lane; rows past lq are dropped by the resource bound.
+    const uint32_t orow = (uint32_t)my_q * qrow_bytes;
 #pragma unroll
-  for (int j = 0; j < 32 * KCH / 64; ++j) {
-    const int c = l + 64 * j;
-    const int row = c / KCH, x = c - row * KCH;
-    const u32x4 v = *(const u32x4*)(st + swz<DP>(row, 8 * x));
-    // rows past lq are dropped by the resource bound
-    buf_store16(v, dq_rs, 8 * x < p.d ? (uint32_t)(qw0 + row) * qrow_bytes + 16u * x : kOobOffset, 0);
+    for (int dt = 0; dt < ND; ++dt)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dd = 32 * dt + 8 * g + 4 * h;
+        u32x2 out;
+        out[0] = (uint32_t)DT::bits(acc[dt][4 * g + 0] * p.scale) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 1] * p.scale) << 16);
+        out[1] = (uint32_t)DT::bits(acc[dt][4 * g + 2] * p.scale) |
+                 ((uint32_t)DT::bits(acc[dt][4 * g + 3] * p.scale) << 16);
+        if (dd < p.d) buf_store8(out, dq_rs, orow + 2u * dd, 0);
+      }
   }
 }
 

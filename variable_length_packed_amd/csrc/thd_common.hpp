@@ -184,7 +184,11 @@ __device__ __forceinline__ void buf_load_lds16(u32x4 rs, uint32_t lds_wave, uint
 }
 #pragma clang diagnostic pop
 
-// 16 bytes per lane (the kernels' outputs are stored as whole rows)
+// 8 or 16 bytes per lane (outputs leave as whole rows staged in LDS, 16 bytes
+// per lane; the 8-byte form stores straight from MFMA accumulators)
+__device__ __forceinline__ void buf_store8(u32x2 v, rsrc_t r, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, (int)voff, (int)soff, 0);
+}
 __device__ __forceinline__ void buf_store16(u32x4 v, rsrc_t r, uint32_t voff, uint32_t soff) {
   __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)voff, (int)soff, 0);
 }
