@@ -1,8 +1,9 @@
 """Benchmark: packed-thd attention forward + backward on one MI355X.
 
 One step = the whole hot path over one synthetic packed batch: the two
-padding masks (query and key side), thd_attn_fwd and thd_attn_bwd, all on
-the current stream with inputs already resident in HBM.  Workload: 16 causal
+padding masks (query and key side, one thd_padding_masks launch), thd_attn_fwd
+and thd_attn_bwd, all on the current stream with inputs already resident in
+HBM.  Workload: 16 causal
 sequences with lengths uniform in [64, 2048] (seed 2, 16,640 tokens), 16
 heads, head_dim 128, bf16, dO ~ N(0,1).
 
@@ -225,10 +226,8 @@ def main():
     def step(i):
         evs = events[i]
         evs[6].record(cur)
-        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], stream),
-                   "mask q")
-        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], stream),
-                   "mask kv")
+        _lib.check(lib.thd_padding_masks(P["cu_q"], P["cu_kv"], w.batch, w.max_seqlen_q,
+                                         w.max_seqlen_kv, P["mq"], P["mkv"], stream), "masks")
         evs[0].record(cur)
         _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
                                     fws_bytes, stream), "fwd")
@@ -241,10 +240,8 @@ def main():
 
     def untimed_step(st=None):
         st = stream if st is None else st
-        _lib.check(lib.thd_padding_mask(P["cu_q"], w.batch, w.max_seqlen_q, P["mq"], st),
-                   "mask q")
-        _lib.check(lib.thd_padding_mask(P["cu_kv"], w.batch, w.max_seqlen_kv, P["mkv"], st),
-                   "mask kv")
+        _lib.check(lib.thd_padding_masks(P["cu_q"], P["cu_kv"], w.batch, w.max_seqlen_q,
+                                         w.max_seqlen_kv, P["mq"], P["mkv"], st), "masks")
         _lib.check(lib.thd_attn_fwd(args, P["q"], P["k"], P["v"], P["o"], P["lse"], P["fws"],
                                     fws_bytes, st), "fwd")
         if a.fwd_only:

@@ -119,6 +119,17 @@ typedef struct {
 int thd_padding_mask(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqlen,
                      uint8_t* mask, void* stream);
 
+/* The query and key/value padding masks [M] (Changes: attention_mask_q and
+ * attention_mask_kv) in one launch: mask_q as thd_padding_mask(cu_seqlens_q,
+ * batch, max_seqlen_q) and mask_kv as thd_padding_mask(cu_seqlens_kv, batch,
+ * max_seqlen_kv), byte for byte.  A mask with batch * max_seqlen = 0 is not
+ * written and its pointers may be NULL.
+ * Errors: THD_ERR_SHAPE (batch or a max_seqlen < 0), THD_ERR_NULL (a
+ * cu_seqlens or mask NULL for a mask with bytes to write). */
+int thd_padding_masks(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                      int32_t max_seqlen_q, int32_t max_seqlen_kv, uint8_t* mask_q,
+                      uint8_t* mask_kv, void* stream);
+
 /* Bytes of device workspace thd_attn_fwd needs for these arguments (the
  * order in which its workgroups take the query tiles, a few bytes per tile),
  * 0 if the arguments are invalid or the batch is empty.  The workspace needs

@@ -166,6 +166,21 @@ def test_padding_mask_host_checks():
     assert lib.thd_padding_mask(None, 3, 0, None, None) == 0
 
 
+def test_padding_mask_pair_host_checks():
+    lib = _lib.load()
+    m = lib.thd_padding_masks
+    assert m(P, P, -1, 4, 4, P, P, None) == -2
+    assert m(P, P, 2, -1, 4, P, P, None) == -2
+    assert m(P, P, 2, 4, -1, P, P, None) == -2
+    assert m(None, P, 2, 4, 4, P, P, None) == -1
+    assert m(P, None, 2, 4, 4, P, P, None) == -1
+    assert m(P, P, 2, 4, 4, None, P, None) == -1
+    assert m(P, P, 2, 4, 4, P, None, None) == -1
+    # a mask with no bytes needs no pointers; with none at all nothing launches
+    assert m(None, None, 0, 4, 4, None, None, None) == 0
+    assert m(None, None, 3, 0, 0, None, None, None) == 0
+
+
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(ImportError):
         _lib.load(str(tmp_path / "libthdattn.so"))

@@ -111,3 +111,41 @@ def test_large_mask_config5_shape():
         got = gpu_mask(np.asarray(cu), w.batch, mx)
         assert got.shape == (32, 1, 1, mx)
         np.testing.assert_array_equal(got, padding_mask(cu, w.batch, mx))
+
+
+@pytest.mark.parametrize("mq,mk,batch", [(512, 8192, 32), (7, 3, 5), (1, 1, 1), (0, 9, 3), (6, 0, 2)])
+def test_mask_pair_in_one_launch(mq, mk, batch):
+    # both masks of a query / key pair from one entry point, each bit-exact
+    # against the definition, with no byte written past either mask
+    rng = np.random.default_rng(mq * 31 + mk)
+    lq = rng.integers(-2, max(mq, 1) + 3, size=batch)
+    lk = rng.integers(-2, max(mk, 1) + 3, size=batch)
+    cu_q, cu_k = _cu(lq, extra=2), _cu(lk, extra=3)
+    print(f"case mq={mq} mk={mk} batch={batch}", flush=True)
+    G = 64
+    bq = torch.full((batch * mq + 2 * G,), 0xAB, dtype=torch.uint8, device="cuda")
+    bk = torch.full((batch * mk + 2 * G,), 0xCD, dtype=torch.uint8, device="cuda")
+    from variable_length_packed_amd import _lib
+    import ctypes
+    lib = _lib.load()
+    tq, tk = torch.from_numpy(cu_q).cuda(), torch.from_numpy(cu_k).cuda()
+    vp = lambda t, off=0: ctypes.c_void_p(t.data_ptr() + off)
+    st = lib.thd_padding_masks(vp(tq), vp(tk), batch, mq, mk, vp(bq, G), vp(bk, G),
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    assert st == 0
+    oq, ok = bq.cpu().numpy(), bk.cpu().numpy()
+    assert np.all(oq[:G] == 0xAB) and np.all(oq[G + batch * mq:] == 0xAB)
+    assert np.all(ok[:G] == 0xCD) and np.all(ok[G + batch * mk:] == 0xCD)
+    if mq:
+        np.testing.assert_array_equal(oq[G:G + batch * mq].reshape(batch, mq),
+                                      padding_mask(cu_q, batch, mq).reshape(batch, mq))
+    if mk:
+        np.testing.assert_array_equal(ok[G:G + batch * mk].reshape(batch, mk),
+                                      padding_mask(cu_k, batch, mk).reshape(batch, mk))
+    if mq and mk:
+        # the torch wrapper gives the same pair
+        gq, gk = thd.padding_masks(tq, tk, batch, mq, mk)
+        np.testing.assert_array_equal(gq.cpu().numpy().reshape(batch, mq),
+                                      oq[G:G + batch * mq].reshape(batch, mq).astype(bool))
+        np.testing.assert_array_equal(gk.cpu().numpy().reshape(batch, mk),
+                                      ok[G:G + batch * mk].reshape(batch, mk).astype(bool))

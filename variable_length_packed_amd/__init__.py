@@ -12,6 +12,7 @@ from .attention import (  # noqa: F401
     bwd_workspace_size,
     fwd_workspace_size,
     padding_mask,
+    padding_masks,
     thd_attention,
 )
 from .metrics import valid_pairs, attention_flops  # noqa: F401

@@ -29,6 +29,7 @@ STATUS = {
 # Every entry point declared in include/thd_attn.h.
 EXPORTED = (
     "thd_padding_mask",
+    "thd_padding_masks",
     "thd_attn_fwd_workspace_size",
     "thd_attn_fwd",
     "thd_attn_fwd_noalloc",
@@ -85,6 +86,8 @@ def load(path=None):
     argsp = ctypes.POINTER(ThdVarlenArgs)
     lib.thd_padding_mask.argtypes = [vp, i32, i32, vp, vp]
     lib.thd_padding_mask.restype = ctypes.c_int
+    lib.thd_padding_masks.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.thd_padding_masks.restype = ctypes.c_int
     lib.thd_attn_fwd_workspace_size.argtypes = [argsp]
     lib.thd_attn_fwd_workspace_size.restype = sz
     lib.thd_attn_fwd.argtypes = [argsp, vp, vp, vp, vp, vp, vp, sz, vp]

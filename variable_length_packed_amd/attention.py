@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["padding_mask", "attn_fwd", "attn_bwd", "bwd_workspace_size", "thd_attention"]
+__all__ = ["padding_mask", "padding_masks", "attn_fwd", "attn_bwd", "bwd_workspace_size", "thd_attention"]
 
 _DTYPES = {torch.float16: _lib.THD_FP16, torch.bfloat16: _lib.THD_BF16}
 
@@ -80,6 +80,31 @@ def padding_mask(cu_seqlens, batch_size, max_seqlen):
                               _stream(cu_seqlens.device))
     _lib.check(st, "thd_padding_mask")
     return mask
+
+
+def padding_masks(cu_seqlens_q, cu_seqlens_kv, batch_size, max_seqlen_q, max_seqlen_kv):
+    """The query and key/value masks of ``padding_mask`` ([batch_size, 1, 1,
+    max_seqlen_q] and [batch_size, 1, 1, max_seqlen_kv]) built by one kernel
+    launch -- the attention_mask_q / attention_mask_kv pair of
+    TransformerEngine PR "[PyTorch] Build the attention padding mask without
+    host syncs"."""
+    _require_cuda("cu_seqlens_q", cu_seqlens_q, torch.int32)
+    _require_cuda("cu_seqlens_kv", cu_seqlens_kv, torch.int32, device=cu_seqlens_q.device)
+    batch_size = int(batch_size)
+    max_seqlen_q, max_seqlen_kv = int(max_seqlen_q), int(max_seqlen_kv)
+    if batch_size < 0 or max_seqlen_q < 0 or max_seqlen_kv < 0:
+        raise ValueError("batch_size and the max_seqlens must be >= 0")
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_kv", cu_seqlens_kv)):
+        if batch_size > 0 and cu.numel() < batch_size + 1:
+            raise ValueError(f"{name} needs at least batch_size + 1 entries")
+    dev = cu_seqlens_q.device
+    mq = torch.empty((batch_size, 1, 1, max_seqlen_q), dtype=torch.bool, device=dev)
+    mkv = torch.empty((batch_size, 1, 1, max_seqlen_kv), dtype=torch.bool, device=dev)
+    lib = _lib.load()
+    st = lib.thd_padding_masks(_ptr(cu_seqlens_q), _ptr(cu_seqlens_kv), batch_size, max_seqlen_q,
+                               max_seqlen_kv, _ptr(mq), _ptr(mkv), _stream(dev))
+    _lib.check(st, "thd_padding_masks")
+    return mq, mkv
 
 
 def _make_args(q, k, cu_q, cu_kv, max_q, max_kv, cu_q_pad, cu_kv_pad, is_causal,

@@ -148,6 +148,20 @@ int thd_padding_mask(const int32_t* cu_seqlens, int32_t batch, int32_t max_seqle
   return e == hipSuccess ? THD_OK : THD_ERR_HIP;
 }
 
+int thd_padding_masks(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_kv, int32_t batch,
+                      int32_t max_seqlen_q, int32_t max_seqlen_kv, uint8_t* mask_q,
+                      uint8_t* mask_kv, void* stream) {
+  if (batch < 0 || max_seqlen_q < 0 || max_seqlen_kv < 0) return THD_ERR_SHAPE;
+  const bool any_q = (int64_t)batch * max_seqlen_q > 0;
+  const bool any_kv = (int64_t)batch * max_seqlen_kv > 0;
+  if ((any_q && (!cu_seqlens_q || !mask_q)) || (any_kv && (!cu_seqlens_kv || !mask_kv)))
+    return THD_ERR_NULL;
+  hipError_t e = thd::launch_padding_masks(cu_seqlens_q, cu_seqlens_kv, batch,
+                                           any_q ? max_seqlen_q : 0, any_kv ? max_seqlen_kv : 0,
+                                           mask_q, mask_kv, (hipStream_t)stream);
+  return e == hipSuccess ? THD_OK : THD_ERR_HIP;
+}
+
 size_t thd_attn_fwd_workspace_size(const thd_varlen_args* args) {
   thd::Problem p;
   if (to_problem(args, &p) != THD_OK) return 0;

@@ -24,6 +24,9 @@ struct Problem {
 
 hipError_t launch_padding_mask(const int32_t* cu, int batch, int max_seqlen, uint8_t* mask,
                                hipStream_t s);
+hipError_t launch_padding_masks(const int32_t* cu_q, const int32_t* cu_kv, int batch,
+                                int max_q, int max_kv, uint8_t* mask_q, uint8_t* mask_kv,
+                                hipStream_t s);
 
 size_t fwd_workspace_bytes(const Problem& p);
 
