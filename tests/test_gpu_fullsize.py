@@ -5,8 +5,9 @@ alone); dk/dv of the shortest sequence, the one with the most query rows and
 the one with the most keys -- whole when the oracle is cheap, else the first,
 a middle and the last 256-key tile over every query head of one kv head (the
 oracle takes such a key range by query-row blocks); and every pad row
-bit-exact +0.  The same checks run on config 2's lengths at head dims 192 and
-256 (fewer heads), so that the 256-wide kernels walk full-length sequences."""
+bit-exact +0.  The same checks run on config 2's lengths at head dims 32, 64,
+96, 192 and 256 (fewer heads), so that every tile shape walks full-length
+sequences."""
 import numpy as np
 import pytest
 import torch
@@ -116,8 +117,8 @@ def test_full_size_config(name):
 
 
 def wide_head_config(d, dtype):
-    """Config 2's lengths (16 causal sequences of 64 to 2,048 tokens) at a
-    head dim above 128, 4 query heads over 2 kv heads."""
+    """Config 2's lengths (16 causal sequences of 64 to 2,048 tokens) at
+    another head dim, 4 query heads over 2 kv heads."""
     rng = np.random.default_rng(2)
     lens = rng.integers(64, 2048, size=16, endpoint=True)
     return workloads.packed(lens, causal=np.ones(16, np.uint8), h_q=4, h_kv=2, d=d,
@@ -125,7 +126,10 @@ def wide_head_config(d, dtype):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("d,dtype", [(192, "bf16"), (256, "fp16"), (256, "bf16")])
-def test_full_length_wide_heads(d, dtype):
-    # the backward's 256-wide passes walk up to 2,034 rows per key tile here
+@pytest.mark.parametrize("d,dtype", [(192, "bf16"), (256, "fp16"), (256, "bf16"),
+                                     (32, "bf16"), (64, "fp16"), (96, "bf16")])
+def test_full_length_other_head_dims(d, dtype):
+    # every tile shape walks full-length sequences (up to 2,034 rows per key
+    # tile): 64-key tiles at d = 32, the three-wave dq pass at d = 64, d = 96
+    # padded to 128, and the 256-wide passes
     check_config(f"2-d{d}", w=wide_head_config(d, dtype))
