@@ -27,6 +27,12 @@ class _StubLib:
     def thd_attn_bwd(self, *args):
         raise _Launched("thd_attn_bwd")
 
+    def thd_padding_mask(self, *args):
+        raise _Launched("thd_padding_mask")
+
+    def thd_padding_masks(self, *args):
+        raise _Launched("thd_padding_masks")
+
 
 @pytest.fixture
 def host(monkeypatch):
@@ -107,3 +113,26 @@ def test_metadata_must_be_int32_on_the_same_device(host):
         attention.attn_fwd(q, k, v, cu_q.long(), cu_kv, 7, 6)
     with pytest.raises(ValueError):
         attention.attn_fwd(q, k, v, cu_q, cu_kv.to("meta"), 7, 6)
+
+
+@pytest.mark.parametrize("kw,exc", [
+    (dict(batch_size=-1), ValueError),
+    (dict(max_seqlen_q=-2), ValueError),
+    (dict(max_seqlen_kv=-1), ValueError),
+    (dict(cu_seqlens_q=torch.tensor([0, 5], dtype=torch.int32)), ValueError),   # too short
+    (dict(cu_seqlens_kv=torch.tensor([0, 4, 10], dtype=torch.int64)), TypeError),
+])
+def test_mask_pair_rejects_bad_arguments_before_launch(host, kw, exc):
+    args = dict(cu_seqlens_q=torch.tensor([0, 5, 12], dtype=torch.int32),
+                cu_seqlens_kv=torch.tensor([0, 4, 10], dtype=torch.int32),
+                batch_size=2, max_seqlen_q=7, max_seqlen_kv=6)
+    args.update(kw)
+    with pytest.raises(exc):
+        attention.padding_masks(**args)
+
+
+def test_mask_pair_valid_arguments_reach_the_launch(host):
+    with pytest.raises(_Launched, match="thd_padding_masks"):
+        attention.padding_masks(torch.tensor([0, 5, 12], dtype=torch.int32),
+                                torch.tensor([0, 4, 10], dtype=torch.int32), 2, 7, 6)
+
