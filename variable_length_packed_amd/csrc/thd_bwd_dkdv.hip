@@ -267,9 +267,12 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
       if (__builtin_expect(need_mask, 0)) {
         const int lim_lo = causal ? my_k - q0 - off : -1;
         const int row_hi = my_k < lk ? lq - q0 : 0;
+        // the rows' offset formed here: hoisted out of the walk, the 16 row
+        // indices held 15 more VGPRs (at d = 64 the third wave per SIMD)
+        const int h4 = (int)opaque(4u * h);
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int qi = 8 * (i >> 2) + 4 * h + (i & 3);
+          const int qi = 8 * (i >> 2) + h4 + (i & 3);
           if (!(qi >= lim_lo && qi < row_hi)) s[nb][i] = -__builtin_inff();
         }
       }
