@@ -20,7 +20,8 @@
  * Conventions common to every entry point
  *   - Every tensor pointer is a DEVICE pointer; the caller allocates and owns
  *     all memory, the library allocates and frees nothing and keeps no state
- *     besides its loaded code objects.
+ *     besides its loaded code objects and the fixed per-device workspace
+ *     array of thd_attn_fwd_noalloc (with its per-device address).
  *   - Tensors are dense and row-major: q, o, dq, dout are [total_q, h_q, d];
  *     k, v, dk, dv are [total_kv, h_kv, d]; row stride h*d elements.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
