@@ -4,8 +4,8 @@
 // One workgroup per (sequence, key tile of BK = 256 or 128 keys, kv head), in
 // schedule order, kv heads minor.  Each wave owns NB blocks of 32 keys and keeps dK^T and dV^T for
 // them in registers (K and V sit in LDS) while the workgroup walks the 32-row
-// query tiles (from the diagonal when causal) of every query head of its GQA
-// group.  Per query tile and key block: S = Q K^T and dP = dO V^T
+// query tiles its keys can see (down to the diagonal when causal), from the
+// last one down, every query head of its GQA group at each tile.  Per query tile and key block: S = Q K^T and dP = dO V^T
 // (accumulators starting from -LSE/scale and -D), P = exp2(S scale log2e),
 // dS = P dP, dV^T += dO^T P and dK^T += Q^T dS (Q^T, dO^T from transpose
 // reads).  With NB > 1 a wave's operand reads of Q, dO, Q^T and dO^T serve
@@ -168,12 +168,19 @@ void thd_bwd_dkdv_kernel(SplitParams p) {
   const uint32_t b_k = swz<DP>(32 * NB * w + r, 8 * h);
   const uint32_t b_t = swz<DP>(4 * h + (g16 >> 2), 16 * (grp & 1) + 4 * (g16 & 3));
 
-  int hq = hk * p.group, q0 = q_start;
+  // Walk order: from the last query tile down to the first one the keys
+  // see, every query head of the group at each tile before the next tile.
+  // The key tiles of a sequence and kv head that run together (on one XCD)
+  // then read the same Q / dO rows at about the same time.
+  const int hq_first = hk * p.group, hq_last = hq_first + p.group - 1;
+  const int q_last = n_qt > 0 ? q_start + (n_qt - 1) * BQ : q_start;
+  int hq = hq_first, q0 = q_last;
   auto advance = [&](int& hq_, int& q0_) {
-    q0_ += BQ;
-    if (q0_ >= lq) {
-      q0_ = q_start;
+    if (hq_ < hq_last) {
       ++hq_;
+    } else {
+      hq_ = hq_first;
+      q0_ -= BQ;
     }
   };
 

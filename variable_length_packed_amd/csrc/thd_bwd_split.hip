@@ -13,7 +13,8 @@
 //               head), 32 keys per wave (128-key tiles of 4 waves for short
 //               walks and for head dims above 128, 256-key tiles of 8 waves
 //               for long ones), walks the
-//               32-row query tiles of every query head of its GQA group,
+//               32-row query tiles of every query head of its GQA group
+//               (from the last tile down, the group's heads innermost),
 //               recomputes S and dP and accumulates dK^T and dV^T in
 //               registers (thd_bwd_dkdv.hip).
 // Textbook softmax-attention backward with the probabilities recomputed from
