@@ -7,13 +7,15 @@ a middle and the last 256-key tile over every query head of one kv head (the
 oracle takes such a key range by query-row blocks); and every pad row
 bit-exact +0.  The same checks run on config 2's lengths at head dims 32, 64,
 96, 192 and 256 (fewer heads), so that every tile shape walks full-length
-sequences."""
+sequences.  On the workloads whose per-head oracle takes about a second
+(configs 2, 3, 5 and 6), every valid row of one kv head and its query heads
+is compared too: output, LSE, dq, dk and dv over every sequence."""
 import numpy as np
 import pytest
 import torch
 
 import workloads
-from oracle import attn_bwd, attn_bwd_key_range, attn_rows
+from oracle import attn_bwd, attn_bwd_key_range, attn_fwd, attn_rows
 from gpu_helpers import assert_close, assert_pad_rows_zero, dev_meta, gpu_bwd, gpu_fwd
 
 pytestmark = pytest.mark.gpu
@@ -133,3 +135,43 @@ def test_full_length_other_head_dims(d, dtype):
     # tile): 64-key tiles at d = 32, the three-wave dq pass at d = 64, d = 96
     # padded to 128, and the 256-wide passes
     check_config(f"2-d{d}", w=wide_head_config(d, dtype))
+
+
+@pytest.mark.parametrize("name", ["2", "3", "5", "6"])
+def test_full_size_whole_head(name):
+    """Every valid row of one kv head and its query heads, at full size and in
+    the benchmark's launch configuration, against the oracle run on that head
+    slice of the whole packed layout (the slice is a layout of its own: the
+    same cu_seqlens, padded offsets and mask types, h_kv = 1)."""
+    w = workloads.config(name)
+    print(f"config {name} whole head: B={w.batch} Tq={w.T_q} Tkv={w.T_kv} h={w.h_q}/{w.h_kv}",
+          flush=True)
+    q, k, v, do = workloads.make_tensors(w, device="cuda")
+    meta = dev_meta(w)
+    o, lse = gpu_fwd(w, q, k, v, meta)
+    dq, dk, dv = gpu_bwd(w, q, k, v, o, do, lse, meta)
+    torch.cuda.synchronize()
+    group = w.h_q // w.h_kv
+    hk = w.h_kv - 1
+    heads = list(range(hk * group, (hk + 1) * group))
+    f64 = lambda t: t.to("cpu", torch.float64).numpy()
+    Q, G = f64(q[:, heads]), f64(do[:, heads])
+    K, V = f64(k[:, hk:hk + 1]), f64(v[:, hk:hk + 1])
+    args = (w.cu_q, w.cu_kv, w.batch, np.asarray(w.causal)[:w.batch])
+    pads = dict(cu_q_padded=w.cu_q_padded, cu_kv_padded=w.cu_kv_padded)
+    ro, rl = attn_fwd(Q, K, V, *args, **pads)
+    rdq, rdk, rdv = attn_bwd(Q, K, V, G, *args, **pads)
+    vq, vk = w.row_is_valid_q(), w.row_is_valid_kv()
+    got_lse = f64(lse[heads])[:, vq]
+    ref_lse = rl[:, vq]
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin), "rows without a visible key differ"
+    assert np.abs(got_lse[fin] - ref_lse[fin]).max() < 1e-3
+    for nm, got, ref, valid in (("out", o[:, heads], ro, vq), ("dq", dq[:, heads], rdq, vq),
+                                ("dk", dk[:, hk:hk + 1], rdk, vk),
+                                ("dv", dv[:, hk:hk + 1], rdv, vk)):
+        ex, rr = assert_close(f"cfg{name} {nm} kv head {hk}", f64(got)[valid], ref[valid],
+                              w.dtype)
+        print(f"config {name} whole head {nm}: abs error beyond rounding {ex:.2e}, "
+              f"relative rms {rr:.2e}", flush=True)
+    print(f"config {name} whole head: ok", flush=True)
