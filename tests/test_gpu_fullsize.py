@@ -8,8 +8,8 @@ oracle takes such a key range by query-row blocks); and every pad row
 bit-exact +0.  The same checks run on config 2's lengths at head dims 32, 64,
 96, 192 and 256 (fewer heads), so that every tile shape walks full-length
 sequences.  On the workloads whose per-head oracle takes about a second
-(configs 2, 3, 5 and 6), every valid row of one kv head and its query heads
-is compared too: output, LSE, dq, dk and dv over every sequence."""
+(configs 2, 3, 5, 6 and 7), every valid row of one kv head and its query
+heads is compared too: output, LSE, dq, dk and dv over every sequence."""
 import numpy as np
 import pytest
 import torch
@@ -137,7 +137,7 @@ def test_full_length_other_head_dims(d, dtype):
     check_config(f"2-d{d}", w=wide_head_config(d, dtype))
 
 
-@pytest.mark.parametrize("name", ["2", "3", "5", "6"])
+@pytest.mark.parametrize("name", ["2", "3", "5", "6", "7"])
 def test_full_size_whole_head(name):
     """Every valid row of one kv head and its query heads, at full size and in
     the benchmark's launch configuration, against the oracle run on that head
