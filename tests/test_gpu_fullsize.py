@@ -175,3 +175,44 @@ def test_full_size_whole_head(name):
         print(f"config {name} whole head {nm}: abs error beyond rounding {ex:.2e}, "
               f"relative rms {rr:.2e}", flush=True)
     print(f"config {name} whole head: ok", flush=True)
+
+
+def test_full_size_gqa_whole_sequences():
+    """Config 4 (GQA 32/8, 131,072 tokens): every sequence of at most 2,048
+    tokens (22 of its 42), whole, for one kv head and its four query heads --
+    output, LSE, dq, dk and dv against the oracle run on each sequence alone.
+    The longer sequences are checked by key ranges in test_full_size_config."""
+    w = workloads.config("4")
+    print(f"config 4 GQA sequences: B={w.batch} Tq={w.T_q} h={w.h_q}/{w.h_kv}", flush=True)
+    q, k, v, do = workloads.make_tensors(w, device="cuda")
+    meta = dev_meta(w)
+    o, lse = gpu_fwd(w, q, k, v, meta)
+    dq, dk, dv = gpu_bwd(w, q, k, v, o, do, lse, meta)
+    torch.cuda.synchronize()
+    group = w.h_q // w.h_kv
+    hk = 2
+    heads = list(range(hk * group, (hk + 1) * group))
+    sq, sk = w.starts_q(), w.starts_kv()
+    f64 = lambda t: t.to("cpu", torch.float64).numpy()
+    chosen = [b for b in range(w.batch) if 0 < w.lens_q[b] <= 2048]
+    assert len(chosen) >= 16
+    got = {n: [] for n in ("out", "dq", "dk", "dv")}
+    ref = {n: [] for n in got}
+    for b in chosen:
+        lq, lk = int(w.lens_q[b]), int(w.lens_kv[b])
+        qs, ks = slice(sq[b], sq[b] + lq), slice(sk[b], sk[b] + lk)
+        Q, G = f64(q[qs, heads]), f64(do[qs, heads])
+        K, V = f64(k[ks, hk:hk + 1]), f64(v[ks, hk:hk + 1])
+        cu_q, cu_k = np.array([0, lq], np.int32), np.array([0, lk], np.int32)
+        ro, rl = attn_fwd(Q, K, V, cu_q, cu_k, 1, [w.causal[b]])
+        rdq, rdk, rdv = attn_bwd(Q, K, V, G, cu_q, cu_k, 1, [w.causal[b]])
+        assert np.abs(f64(lse[heads][:, qs]) - rl).max() < 1e-3, b
+        for n, g, r in (("out", o[qs, heads], ro), ("dq", dq[qs, heads], rdq),
+                        ("dk", dk[ks, hk:hk + 1], rdk), ("dv", dv[ks, hk:hk + 1], rdv)):
+            got[n].append(f64(g).reshape(-1))
+            ref[n].append(r.reshape(-1))
+    for n in got:
+        ex, rr = assert_close(f"cfg4 {n} of {len(chosen)} sequences, kv head {hk}",
+                              np.concatenate(got[n]), np.concatenate(ref[n]), w.dtype)
+        print(f"config 4 GQA sequences {n}: abs error beyond rounding {ex:.2e}, "
+              f"relative rms {rr:.2e}", flush=True)
