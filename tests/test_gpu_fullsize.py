@@ -129,7 +129,8 @@ def wide_head_config(d, dtype):
 
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("d,dtype", [(192, "bf16"), (256, "fp16"), (256, "bf16"),
-                                     (32, "bf16"), (64, "fp16"), (96, "bf16")])
+                                     (32, "bf16"), (64, "fp16"), (96, "bf16"),
+                                     (128, "fp16")])
 def test_full_length_other_head_dims(d, dtype):
     # every tile shape walks full-length sequences (up to 2,034 rows per key
     # tile): 64-key tiles at d = 32, the three-wave dq pass at d = 64, d = 96
